@@ -1,0 +1,43 @@
+"""Per-tensor current-scaling FP8 (E4M3) oracle.  Test infrastructure.
+
+[HP329] §3.2: the current-scaling recipe takes ``scale = valid(amax) ?
+amax / format_max : 1.0``, held in FP32 and recomputed from the current tensor
+each call.  [FPBLOG] §七.2: per-tensor scaling shares one scale over the whole
+tensor, found by a first pass over it (amax), then a second pass quantizes.
+
+Readings: format_max is E4M3's 448; "valid" means finite and > 0; amax is
+NaN-propagating; the data are ``E4M3_RNE_sat(fp32(x) / scale)`` with an IEEE
+FP32 division (round to nearest even), and dequantization is ``q * scale``.
+"""
+
+import numpy as np
+
+from .codec import E4M3_MAX, bf16_bits_to_f64, e4m3_decode, e4m3_encode
+
+
+def pt_scale(x_bf16_bits):
+    """FP32 scale of a BF16 tensor: fp32(amax) / fp32(448), or 1.0."""
+    x = bf16_bits_to_f64(np.asarray(x_bf16_bits).ravel())
+    if x.size == 0:
+        return np.float32(1.0)
+    a = np.abs(x)
+    amax = np.nan if np.isnan(a).any() else a.max()
+    if not np.isfinite(amax) or amax <= 0:
+        return np.float32(1.0)
+    # amax is a BF16 value, so float32(amax) is exact; the division is FP32.
+    return np.float32(amax) / np.float32(E4M3_MAX)
+
+
+def pt_quantize(x_bf16_bits):
+    """Returns (codes uint8 of x's shape, scale np.float32)."""
+    bits = np.asarray(x_bf16_bits, dtype=np.uint16)
+    s = pt_scale(bits)
+    x32 = bf16_bits_to_f64(bits).astype(np.float32)      # exact
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = x32 / np.float32(s)                          # IEEE FP32, RNE
+    return e4m3_encode(q.astype(np.float64)), np.float32(s)
+
+
+def pt_dequantize(codes, scale):
+    """Exact float64 values q * scale."""
+    return e4m3_decode(codes) * np.float64(np.float32(scale))
