@@ -1,0 +1,443 @@
+// MX (E4M3 + E8M0 per 32 values) and per-tensor FP8 quantization kernels
+// for gfx950, with their C-ABI launchers.
+//
+// Method: "DeepSeek-V3 16B FSDP2 MXFP8/HiF8 训练设计" §3 table (1x32 and 32x1
+// blocks, E8M0 scale from the current block) and §3.2 (current scaling,
+// scale = valid(amax) ? amax / format_max : 1.0 in FP32); "低精度训练特性
+// （MXFP8 / HiFloat8）" (block size 32; grouped quant for the expert wgrad);
+// E4M3 layout from "Transformer 与 LLM（06）：浮点格式、数值稳定性与混合精度" §二.2.
+//
+// All three kernels are HBM-bound streams: 2 bytes read and 1 + 1/32 bytes
+// written per element (MX), or 2 + 2 read and 1 written (per-tensor, two
+// passes).  Loads and stores are 16 B (8 B for codes in the row kernel) per
+// lane and contiguous across the wavefront.
+
+#include "common.h"
+
+#include <algorithm>
+
+namespace mxq {
+
+// ---------------------------------------------------------------------------
+// Row-wise MX quantization.
+//
+// A wavefront owns a segment of 512 consecutive elements of one row; lane l
+// holds elements [8l, 8l+8), so the 4 lanes of a DPP quad hold one 32-element
+// block.  The block amax is a packed-u16 max over the lane's 8 magnitudes and
+// two quad DPP exchanges.  A contiguous matrix is passed as a single row so
+// segments run across row ends.
+// ---------------------------------------------------------------------------
+
+constexpr int kRowUnroll = 4;
+
+__device__ __forceinline__ void quant8(uint4 v, uint32_t& lo, uint32_t& hi, uint32_t& code) {
+  u16x2 m = __builtin_elementwise_max(absmax2(v.x, v.y), absmax2(v.z, v.w));
+  uint32_t am = m.x > m.y ? m.x : m.y;
+  uint32_t o = dpp_u32(am, kQuadXor1);
+  am = am > o ? am : o;
+  o = dpp_u32(am, kQuadXor2);
+  am = am > o ? am : o;
+  code = mx_scale_code(am);
+  if (code == 0xFFu) {                 // NaN or Inf in the block
+    lo = hi = 0x7F7F7F7Fu;
+    return;
+  }
+  float inv = mx_inv_scale(code);      // x * 2^-e is exact in FP32
+  lo = cvt2_e4m3_sat<false>(bf16_lo(v.x) * inv, bf16_hi(v.x) * inv, 0u);
+  lo = cvt2_e4m3_sat<true>(bf16_lo(v.y) * inv, bf16_hi(v.y) * inv, lo);
+  hi = cvt2_e4m3_sat<false>(bf16_lo(v.z) * inv, bf16_hi(v.z) * inv, 0u);
+  hi = cvt2_e4m3_sat<true>(bf16_lo(v.w) * inv, bf16_hi(v.w) * inv, hi);
+}
+
+__global__ __launch_bounds__(256) void k_mx_rowwise(
+    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ sc, int64_t lds, uint32_t K, uint32_t segs_per_row,
+    uint32_t total_segs) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
+  for (uint32_t s0 = wave * kRowUnroll; s0 < total_segs; s0 += nwave * kRowUnroll) {
+    uint4 v[kRowUnroll];
+    uint32_t row[kRowUnroll], col[kRowUnroll];
+    bool ok[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      uint32_t s = s0 + u;
+      row[u] = s / segs_per_row;                    // wave-uniform
+      col[u] = (s - row[u] * segs_per_row) * 512u + lane * 8u;
+      ok[u] = (s < total_segs) && (col[u] < K);
+      v[u] = ok[u] ? *reinterpret_cast<const uint4*>(x + (int64_t)row[u] * ldx + col[u])
+                   : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      uint32_t lo, hi, code;
+      quant8(v[u], lo, hi, code);
+      if (ok[u]) {
+        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + col[u]) = make_uint2(lo, hi);
+        if ((lane & 3u) == 0u) sc[(int64_t)row[u] * lds + (col[u] >> 5)] = (uint8_t)code;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Column-wise (grouped, zero-padded) MX quantization, transposed output.
+//
+// A workgroup (256 lanes) owns 128 consecutive padded output columns (four
+// 32-blocks along M) by 64 input columns (K).  It loads the 128 source rows
+// (16 B per lane, coalesced along K) into LDS, then each wave quantizes one
+// 32-block: lane pair (2p, 2p+1) holds input columns 2p and 2p+1 for the upper
+// and lower 16 rows of the block, takes a packed-u16 max down its 16 rows and
+// one DPP exchange with its partner, and writes 16 codes for each of its two
+// columns as one 16 B store into the transposed output.
+// ---------------------------------------------------------------------------
+
+constexpr int kColTileM = 128;   // padded output columns per workgroup
+constexpr int kColTileK = 64;    // input columns per workgroup
+constexpr int kColLdsW = 34;     // LDS row stride in dwords (32 + 2 pad)
+constexpr int kColMaxGroupsLds = 256;
+
+__global__ __launch_bounds__(256) void k_mx_colwise(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const int64_t* __restrict__ offsets, int32_t E,
+    uint8_t* __restrict__ qT, int64_t ldqT, int64_t M_cap,
+    uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded) {
+  __shared__ uint32_t tile[kColTileM * kColLdsW];
+  __shared__ int64_t s_off[kColMaxGroupsLds + 1];
+  __shared__ int64_t s_poff[kColMaxGroupsLds + 1];
+  __shared__ int64_t s_src0[4];
+  __shared__ int32_t s_nvalid[4];
+
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)blockIdx.x * kColTileM;     // first padded column
+  const int64_t k0 = (int64_t)blockIdx.y * kColTileK;     // first input column
+
+  // Group table: s_off = clamped offsets, s_poff = padded prefix sums.
+  const int G = offsets ? E : 1;
+  for (int g = tid; g <= G; g += blockDim.x) {
+    int64_t o = offsets ? offsets[g] : (g == 0 ? 0 : M);
+    s_off[g] = o < 0 ? 0 : (o > M ? M : o);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // Wave-wide inclusive scan of padded group sizes, 64 groups per step.
+    int64_t carry = 0;
+    if (tid == 0) s_poff[0] = 0;
+    for (int base = 0; base < G; base += 64) {
+      int g = base + tid;
+      int64_t cnt = 0;
+      if (g < G) {
+        int64_t d = s_off[g + 1] - s_off[g];
+        cnt = d > 0 ? (d + 31) / 32 * 32 : 0;
+      }
+      int64_t v = cnt;
+#pragma unroll
+      for (int sh = 1; sh < 64; sh <<= 1) {
+        int64_t t = __shfl_up(v, sh, 64);
+        if (tid >= sh) v += t;
+      }
+      if (g < G) s_poff[g + 1] = carry + v;
+      carry += __shfl(v, 63, 64);
+    }
+  }
+  __syncthreads();
+  if (offsets_padded && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int g = tid; g <= G; g += blockDim.x) offsets_padded[g] = s_poff[g];
+  if (tid < 4) {
+    // Source rows of 32-block tid of this tile: find g with
+    // poff[g] <= col < poff[g+1] (binary search over the non-decreasing poff).
+    int64_t col = p0 + 32 * tid;
+    int64_t src0 = 0;
+    int32_t nvalid = 0;
+    if (col < s_poff[G] && col < M_cap) {
+      int lo = 0, hi = G - 1;
+      while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (s_poff[mid] <= col) lo = mid; else hi = mid - 1;
+      }
+      int64_t r0 = s_off[lo] + (col - s_poff[lo]);
+      int64_t r1 = s_off[lo + 1];
+      src0 = r0;
+      int64_t n = r1 - r0;
+      nvalid = n <= 0 ? 0 : (n >= 32 ? 32 : (int32_t)n);
+    }
+    s_src0[tid] = src0;
+    s_nvalid[tid] = nvalid;
+  }
+  __syncthreads();
+
+  // Load 128 rows x 64 columns (8 chunks of 8 BF16 per row).
+  const int chunk = tid & 7;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    int i = pass * 32 + (tid >> 3);                 // tile row 0..127
+    int b = i >> 5, r = i & 31;
+    int64_t kc = k0 + chunk * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < s_nvalid[b] && kc < K)
+      v = *reinterpret_cast<const uint4*>(x + (s_src0[b] + r) * ldx + kc);
+    *reinterpret_cast<uint4*>(&tile[i * kColLdsW + chunk * 4]) = v;
+  }
+  __syncthreads();
+
+  // Quantize: wave w -> block w; lane = 2p + h: column pair p, row half h.
+  const int w = tid >> 6, lane = tid & 63;
+  const int p = lane >> 1, h = lane & 1;
+  const int rbase = w * 32 + h * 16;
+  uint32_t vals[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) vals[j] = tile[(rbase + j) * kColLdsW + p];
+  u16x2 m = __builtin_bit_cast(u16x2, 0u);
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) m = __builtin_elementwise_max(m, absmax2(vals[j], vals[j + 1]));
+  uint32_t mw = __builtin_bit_cast(uint32_t, m);
+  uint32_t ow = dpp_u32(mw, kQuadXor1);             // partner lane^1: other half
+  u16x2 mm = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ow));
+  uint32_t code0 = mx_scale_code(mm.x);             // column 2p
+  uint32_t code1 = mx_scale_code(mm.y);             // column 2p+1
+  float inv0 = mx_inv_scale(code0 == 0xFFu ? 127u : code0);
+  float inv1 = mx_inv_scale(code1 == 0xFFu ? 127u : code1);
+  uint32_t c0[4], c1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
+    uint32_t t0 = cvt2_e4m3_sat<false>(bf16_lo(a) * inv0, bf16_lo(b2) * inv0, 0u);
+    c0[j] = cvt2_e4m3_sat<true>(bf16_lo(c) * inv0, bf16_lo(d) * inv0, t0);
+    uint32_t t1 = cvt2_e4m3_sat<false>(bf16_hi(a) * inv1, bf16_hi(b2) * inv1, 0u);
+    c1[j] = cvt2_e4m3_sat<true>(bf16_hi(c) * inv1, bf16_hi(d) * inv1, t1);
+  }
+  if (code0 == 0xFFu) c0[0] = c0[1] = c0[2] = c0[3] = 0x7F7F7F7Fu;
+  if (code1 == 0xFFu) c1[0] = c1[1] = c1[2] = c1[3] = 0x7F7F7F7Fu;
+
+  const int64_t col = p0 + w * 32;                  // padded column of this block
+  const int64_t k = k0 + 2 * p;
+  if (col < M_cap && k < K) {
+    int64_t o = col + h * 16;
+    *reinterpret_cast<uint4*>(qT + k * ldqT + o) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+    *reinterpret_cast<uint4*>(qT + (k + 1) * ldqT + o) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+    if (h == 0) {
+      scT[k * ldsT + (col >> 5)] = (uint8_t)code0;
+      scT[(k + 1) * ldsT + (col >> 5)] = (uint8_t)code1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor current scaling: pass 1 reduces |x| to one packed max per
+// workgroup; pass 2 re-reduces the partials (every workgroup, same order, so
+// the result is deterministic), forms s = fp32(amax) / 448 or 1.0, and
+// encodes q = RNE_E4M3(RN(x / s)).  The quotient is the correctly rounded
+// FP32 division, formed as q0 = RN(x * r) with r = RN(1/s) and one FMA
+// correction RN(q0 + RN'(x - s*q0) * r) (Markstein); when s is subnormal the
+// kernel divides directly.
+// ---------------------------------------------------------------------------
+
+constexpr int kPtBlocks = 1024;
+constexpr int kPtThreads = 256;
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, sh, 64);
+    v = v > o ? v : o;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = r > red[i] ? r : red[i];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kPtThreads) void k_pt_amax(const uint16_t* __restrict__ x, int64_t n,
+                                                        uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kPtThreads / 64];
+  const int64_t nchunks = n >> 3;
+  uint32_t m = 0;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = reinterpret_cast<const uint4*>(x)[c];
+    u16x2 mm = __builtin_elementwise_max(absmax2(v.x, v.y), absmax2(v.z, v.w));
+    uint32_t t = mm.x > mm.y ? mm.x : mm.y;
+    m = m > t ? m : t;
+  }
+  // tail (n % 8 elements)
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    uint32_t t = x[(nchunks << 3) + threadIdx.x] & 0x7FFFu;
+    m = m > t ? m : t;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__device__ __forceinline__ float pt_div(float xv, float s, float r, bool direct) {
+  if (direct) return __fdiv_rn(xv, s);
+  float q0 = xv * r;
+  float rem = __builtin_fmaf(-q0, s, xv);
+  // s > 0, so the quotient has the sign of x; the correction step alone
+  // would turn -0 into +0.
+  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), xv);
+}
+
+// Codes of two BF16 values packed in w, for a tensor whose amax is NaN/Inf
+// (s == 1): NaN -> 0x7F|sign, +-Inf -> saturate.
+template <bool HI>
+__device__ __forceinline__ uint32_t pt_nonfinite_pair(uint32_t w, uint32_t old) {
+  uint32_t out = cvt2_e4m3_sat<HI>(bf16_lo(w), bf16_hi(w), old);
+  uint32_t sh = HI ? 16u : 0u;
+  uint32_t b0 = w & 0x7FFFu, b1 = (w >> 16) & 0x7FFFu;
+  if (b0 > 0x7F80u) out = (out & ~(0xFFu << sh)) | ((0x7Fu | ((w >> 8) & 0x80u)) << sh);
+  if (b1 > 0x7F80u) out = (out & ~(0xFFu << (sh + 8))) | ((0x7Fu | ((w >> 24) & 0x80u)) << (sh + 8));
+  return out;
+}
+
+__global__ __launch_bounds__(kPtThreads) void k_pt_quant(const uint16_t* __restrict__ x, int64_t n,
+                                                         const uint32_t* __restrict__ partial, int nparts,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale_out) {
+  __shared__ uint32_t red[kPtThreads / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = m > partial[i] ? m : partial[i];
+  m = block_max_u32(m, red);
+  const bool nonfinite = m >= 0x7F80u;
+  float s = 1.0f;
+  if (!nonfinite && m != 0u) s = __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
+  const bool direct = s < 1.17549435e-38f;        // subnormal scale: divide directly
+  const float r = __frcp_rn(s);
+
+  const int64_t nchunks = n >> 3;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = reinterpret_cast<const uint4*>(x)[c];
+    uint32_t lo, hi;
+    if (nonfinite) {
+      lo = pt_nonfinite_pair<false>(v.x, 0u);
+      lo = pt_nonfinite_pair<true>(v.y, lo);
+      hi = pt_nonfinite_pair<false>(v.z, 0u);
+      hi = pt_nonfinite_pair<true>(v.w, hi);
+    } else {
+      lo = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.x), s, r, direct), pt_div(bf16_hi(v.x), s, r, direct), 0u);
+      lo = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.y), s, r, direct), pt_div(bf16_hi(v.y), s, r, direct), lo);
+      hi = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.z), s, r, direct), pt_div(bf16_hi(v.z), s, r, direct), 0u);
+      hi = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.w), s, r, direct), pt_div(bf16_hi(v.w), s, r, direct), hi);
+    }
+    reinterpret_cast<uint2*>(q)[c] = make_uint2(lo, hi);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    int64_t i = (nchunks << 3) + threadIdx.x;
+    uint32_t w = x[i];
+    uint32_t out = nonfinite ? pt_nonfinite_pair<false>(w, 0u)
+                             : cvt2_e4m3_sat<false>(pt_div(bf16_lo(w), s, r, direct), 0.0f, 0u);
+    q[i] = (uint8_t)(out & 0xFFu);
+  }
+}
+
+__global__ void k_fill_f32(float* p, float v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
+}  // namespace mxq
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+using namespace mxq;
+
+static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+static int num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, uint8_t* scale, int64_t lds,
+                                   hipStream_t stream) {
+  if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return MXQ_OK;
+  if (!x || !q || !scale) return MXQ_ERR_NULL;
+  if (K % 32 != 0 || ldx < K || ldq < K || lds < K / 32) return MXQ_ERR_SHAPE;
+  if (ldx % 8 != 0 || ldq % 16 != 0 || !aligned(x, 16) || !aligned(q, 16)) return MXQ_ERR_ALIGN;
+  // A contiguous matrix is one long row: segments then cross row ends.
+  int64_t rows = M, cols = K;
+  if (ldx == K && ldq == K && lds == K / 32 && M * K <= 0xFFFFFFFFLL) { rows = 1; cols = M * K; }
+  int64_t segs_per_row = (cols + 511) / 512;
+  int64_t total = rows * segs_per_row;
+  if (cols > 0xFFFFFFFFLL || total > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  int64_t waves = (total + kRowUnroll - 1) / kRowUnroll;
+  int64_t blocks = (waves + 3) / 4;
+  int64_t cap = (int64_t)num_cus() * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(k_mx_rowwise, dim3((uint32_t)blocks), dim3(256), 0, stream, x,
+                     rows == 1 ? cols : ldx, q, rows == 1 ? cols : ldq, scale,
+                     rows == 1 ? cols / 32 : lds, (uint32_t)cols, (uint32_t)segs_per_row,
+                     (uint32_t)total);
+  return launch_status();
+}
+
+extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   const int64_t* offsets, int32_t E, uint8_t* qT, int64_t ldqT,
+                                   int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
+                                   int64_t* offsets_padded, hipStream_t stream) {
+  if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (offsets && (E < 1 || E > kColMaxGroupsLds)) return MXQ_ERR_SHAPE;
+  if (K == 0 || M_cap == 0) return MXQ_OK;
+  if (!qT || !scaleT || (M > 0 && !x)) return MXQ_ERR_NULL;
+  if (K % 8 != 0 || M_cap % 32 != 0 || ldqT < M_cap || ldsT < M_cap / 32 || ldx < K)
+    return MXQ_ERR_SHAPE;
+  int64_t need = offsets ? M + 31LL * E : (M + 31) / 32 * 32;
+  if (!offsets && M_cap < need) return MXQ_ERR_SHAPE;
+  (void)need;
+  if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
+    return MXQ_ERR_ALIGN;
+  dim3 grid((uint32_t)((M_cap + kColTileM - 1) / kColTileM),
+            (uint32_t)((K + kColTileK - 1) / kColTileK));
+  hipLaunchKernelGGL(k_mx_colwise, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E, qT,
+                     ldqT, M_cap, scaleT, ldsT, offsets_padded);
+  return launch_status();
+}
+
+extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t, int64_t, int64_t) {
+  if (op == MXQ_WS_PER_TENSOR) return n > 0 ? kPtBlocks * sizeof(uint32_t) : 0;
+  return 0;
+}
+
+extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (n < 0) return MXQ_ERR_SHAPE;
+  if (!scale) return MXQ_ERR_NULL;
+  if (n == 0) {
+    // Empty tensor: no amax to take, the scale is 1.0.
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, stream, scale, 1.0f);
+    return launch_status();
+  }
+  if (!x || !q || !workspace) return MXQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(workspace, 4)) return MXQ_ERR_ALIGN;
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_TENSOR, n, 0, 0, 0)) return MXQ_ERR_WORKSPACE;
+  int64_t chunks = n / 8;
+  int64_t blocks = (chunks + kPtThreads - 1) / kPtThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > kPtBlocks) blocks = kPtBlocks;
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  hipLaunchKernelGGL(k_pt_amax, dim3((uint32_t)blocks), dim3(kPtThreads), 0, stream, x, n, partial);
+  int st = launch_status();
+  if (st != MXQ_OK) return st;
+  hipLaunchKernelGGL(k_pt_quant, dim3((uint32_t)blocks), dim3(kPtThreads), 0, stream, x, n,
+                     partial, (int)blocks, q, scale);
+  return launch_status();
+}

@@ -1,0 +1,236 @@
+"""ctypes binding of libmxq.so.
+
+Argument marshalling only: every function below checks nothing itself,
+allocates its outputs with torch (device memory is the caller's), passes raw
+device pointers and the current HIP stream to the C function of the same
+name, and raises if the library returns an error.  All arithmetic happens in
+the library's HIP kernels; there is no other code path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+OUT_BF16, OUT_FP32 = 0, 1
+ACC_MFMA_FP8, ACC_FP32 = 0, 1
+WS_PER_TENSOR = 0
+
+_i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGS = {
+    "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mxq_version": (ctypes.c_int, []),
+    "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _i64,
+                                           _p, _i64, _p, _p]),
+    "fp8_quantize_per_tensor": (ctypes.c_int, [_p, _i64, _p, _p, _p, _sz, _p]),
+    "mx_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64,
+                               _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
+    "fp8_gemm_per_tensor": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
+                                           _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
+    "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _i32,
+                                       _i64, _i64, _i64, _p, _i64, ctypes.c_int,
+                                       ctypes.c_int, _p]),
+    "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p,
+                                             _i32, _i64, _i64, _p, _i64, ctypes.c_int,
+                                             ctypes.c_int, _p]),
+    "mxq_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, _i64, _i64]),
+    "mxq_validate_offsets": (ctypes.c_int, [_p, _i32, _i64, _p]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class MxqError(RuntimeError):
+    pass
+
+
+def load(path=LIB_PATH):
+    """Load libmxq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise MxqError(f"{path} is missing: build it with "
+                           "`python -m block_quant_gemm_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        msg = load().mxq_status_string(status).decode()
+        raise MxqError(f"libmxq error {status}: {msg}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _bf16_bits(x):
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError("expected a bfloat16 tensor (or its 16-bit patterns)")
+
+
+# ---------------------------------------------------------------------------
+# quantization
+# ---------------------------------------------------------------------------
+
+def mx_quantize_rowwise(x, q=None, scale=None):
+    """Row-wise (1x32) MX quantization of a BF16 [M, K] matrix.
+
+    Returns (codes uint8 [M, K], scales uint8 [M, K/32])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(load().mx_quantize_rowwise(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0),
+                                      _ptr(scale), scale.stride(0), _stream()))
+    return q, scale
+
+
+def colwise_capacity(M, E=None):
+    """Output columns that hold any padding of M rows over E groups, rounded
+    up to a multiple of 128."""
+    need = M + 31 * E if E else (M + 31) // 32 * 32
+    return (need + 127) // 128 * 128
+
+
+def mx_quantize_colwise(x, offsets=None, M_cap=None, qT=None, scaleT=None,
+                        offsets_padded=None):
+    """Column-wise (32x1) MX quantization, transposed: returns
+    (codesT uint8 [K, M_cap], scalesT uint8 [K, M_cap/32], offsets_padded or None).
+
+    With ``offsets`` (int64 [E+1] on the device) each group of rows is padded
+    to a multiple of 32 with zeros; ``offsets_padded`` receives the padded
+    group starts."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = 0 if offsets is None else offsets.numel() - 1
+    if M_cap is None:
+        M_cap = colwise_capacity(M, E or None)
+    if qT is None:
+        qT = torch.empty((K, M_cap), dtype=torch.uint8, device=x.device)
+    if scaleT is None:
+        scaleT = torch.empty((K, M_cap // 32), dtype=torch.uint8, device=x.device)
+    if offsets is not None and offsets_padded is None:
+        offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
+    _check(load().mx_quantize_colwise(_ptr(x), M, K, x.stride(0), _ptr(offsets), E,
+                                      _ptr(qT), qT.stride(0), M_cap, _ptr(scaleT),
+                                      scaleT.stride(0), _ptr(offsets_padded), _stream()))
+    return qT, scaleT, offsets_padded
+
+
+def workspace_size(op, n, a1=0, a2=0, a3=0):
+    return int(load().mxq_workspace_size(op, n, a1, a2, a3))
+
+
+def fp8_quantize_per_tensor(x, q=None, scale=None, workspace=None):
+    """Per-tensor current-scaling E4M3.  Returns (codes uint8, scale float32 [1])."""
+    x = _bf16_bits(x)
+    n = x.numel()
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace_size(WS_PER_TENSOR, n)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=x.device)
+    _check(load().fp8_quantize_per_tensor(_ptr(x), n, _ptr(q), _ptr(scale), _ptr(workspace),
+                                          workspace.numel(), _stream()))
+    return q, scale
+
+
+# ---------------------------------------------------------------------------
+# GEMMs
+# ---------------------------------------------------------------------------
+
+def _out(M, N, out_dtype, device, c):
+    if c is not None:
+        return c
+    dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
+    return torch.empty((M, N), dtype=dt, device=device)
+
+
+def mx_gemm(a, a_scale, b, b_scale, out_dtype=OUT_BF16, accum=ACC_MFMA_FP8, c=None):
+    """C[M, N] = A[M, K] · B[N, K]ᵀ on MX operands (codes + E8M0 scales)."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = _out(M, N, out_dtype, a.device, c)
+    _check(load().mx_gemm(_ptr(a), _ptr(a_scale), a.stride(0), a_scale.stride(0),
+                          _ptr(b), _ptr(b_scale), b.stride(0), b_scale.stride(0),
+                          M, N, K, _ptr(c), c.stride(0), out_dtype, accum, _stream()))
+    return c
+
+
+def fp8_gemm_per_tensor(a, a_scale, b, b_scale, out_dtype=OUT_BF16, accum=ACC_MFMA_FP8,
+                        c=None):
+    """C = s_a * s_b * (Q_a · Q_bᵀ); a_scale, b_scale: float32 [1] on the device."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = _out(M, N, out_dtype, a.device, c)
+    _check(load().fp8_gemm_per_tensor(_ptr(a), _ptr(a_scale), a.stride(0), _ptr(b),
+                                      _ptr(b_scale), b.stride(0), M, N, K, _ptr(c),
+                                      c.stride(0), out_dtype, accum, _stream()))
+    return c
+
+
+def mx_grouped_gemm(a, a_scale, b, b_scale, offsets, out_dtype=OUT_BF16,
+                    accum=ACC_MFMA_FP8, c=None):
+    """Variable-M grouped GEMM: rows [o_e, o_e+1) of A times B[e]ᵀ.
+
+    a [M, K], b [E, N, K] codes with scales [M, K/32], [E, N, K/32];
+    offsets int64 [E+1] on the device."""
+    M, K = a.shape
+    E, N, _ = b.shape
+    c = _out(M, N, out_dtype, a.device, c)
+    _check(load().mx_grouped_gemm(_ptr(a), _ptr(a_scale), a.stride(0), a_scale.stride(0),
+                                  _ptr(b), _ptr(b_scale), b.stride(1), b_scale.stride(1),
+                                  _ptr(offsets), E, M, N, K, _ptr(c), c.stride(0),
+                                  out_dtype, accum, _stream()))
+    return c
+
+
+def mx_grouped_gemm_wgrad(at, at_scale, bt, bt_scale, offsets_padded, out_dtype=OUT_BF16,
+                          accum=ACC_MFMA_FP8, c=None):
+    """Variable-K grouped GEMM: dW[e] = Aᵀ[:, group e] · (Bᵀ[:, group e])ᵀ.
+
+    at [N, T], bt [K, T] column-quantized codes with scales [N, T/32],
+    [K, T/32]; offsets_padded int64 [E+1] (multiples of 32) on the device.
+    Returns dW [E, N, K]."""
+    N = at.shape[0]
+    K = bt.shape[0]
+    E = offsets_padded.numel() - 1
+    if c is None:
+        dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
+        c = torch.empty((E, N, K), dtype=dt, device=at.device)
+    _check(load().mx_grouped_gemm_wgrad(_ptr(at), _ptr(at_scale), at.stride(0),
+                                        at_scale.stride(0), _ptr(bt), _ptr(bt_scale),
+                                        bt.stride(0), bt_scale.stride(0),
+                                        _ptr(offsets_padded), E, N, K, _ptr(c),
+                                        c.stride(1), out_dtype, accum, _stream()))
+    return c
+
+
+def validate_offsets(offsets, M):
+    """Synchronizing check of device offsets (debug aid)."""
+    _check(load().mxq_validate_offsets(_ptr(offsets), offsets.numel() - 1, M, _stream()))

@@ -1,0 +1,206 @@
+"""Bit-exact parity of the HIP quantization kernels with the CPU oracle.
+
+Runs through the C ABI (ctypes binding).  Codes and scales must be equal byte
+for byte, padding included."""
+
+import numpy as np
+import pytest
+import torch
+
+from block_quant_gemm_amd import mxq, workloads
+from oracle import codec, mx, per_tensor
+from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(vals):
+    t = torch.tensor(np.asarray(vals, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+ANCHORS = [2.0 ** -133, 2.0 ** -126, 2.0 ** -119, 2.0 ** -60, 1.0 / 3, 1.0, 255.0,
+           448.0, 3.0e4, 2.0 ** 100, 3.0e38]
+
+
+@pytest.mark.parametrize("anchor", ANCHORS)
+def test_rowwise_every_bf16_pattern(anchor):
+    say(f"rowwise all patterns, anchor {anchor}")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = np.zeros((65536, 32), np.uint16)
+    x[:, 0] = bf16([anchor])[0]
+    x[:, 1] = pats
+    x[:, 2] = pats[::-1]
+    q, s = mxq.mx_quantize_rowwise(to_dev_bf16(x))
+    torch.cuda.synchronize()
+    rc, rs = mx.mx_quantize_rowwise(x)
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rc)
+
+
+def test_rowwise_tiny_linear():
+    d = workloads.tiny_linear(0)
+    for name in ("A", "W"):
+        q, s = mxq.mx_quantize_rowwise(to_dev_bf16(d[name]))
+        rc, rs = mx.mx_quantize_rowwise(d[name])
+        assert np.array_equal(host(q), rc) and np.array_equal(host(s), rs), name
+
+
+def test_rowwise_dense_ffn_full_size():
+    say("rowwise dense FFN X 8192x2048, W 10944x2048")
+    d = workloads.dense_ffn(0)
+    for name in ("X", "W"):
+        q, s = mxq.mx_quantize_rowwise(to_dev_bf16(d[name]))
+        rc, rs = mx.mx_quantize_rowwise(d[name])
+        assert np.array_equal(host(s), rs), name
+        assert np.array_equal(host(q), rc), name
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (37, 96), (5, 544), (130, 1408)])
+def test_rowwise_strided_ragged(M, K):
+    say(f"rowwise strided M={M} K={K}")
+    ldx = K + 24
+    big = workloads.bf16_normal((M, ldx), 1.0, seed=M, name="rs", outlier_frac=0.02,
+                                outlier_scale=80.0)
+    xd = to_dev_bf16(big)[:, :K]
+    ldq = (K + 16 + 15) // 16 * 16
+    qbuf = torch.full((M, ldq), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((M, K // 32 + 3), 0xCD, dtype=torch.uint8, device="cuda")
+    mxq.mx_quantize_rowwise(xd, qbuf[:, :K], sbuf[:, :K // 32])
+    rc, rs = mx.mx_quantize_rowwise(np.ascontiguousarray(big[:, :K]))
+    qh, sh = host(qbuf), host(sbuf)
+    assert np.array_equal(qh[:, :K], rc) and np.array_equal(sh[:, :K // 32], rs)
+    assert np.all(qh[:, K:] == 0xAB) and np.all(sh[:, K // 32:] == 0xCD)   # untouched
+
+
+def test_rowwise_special_blocks():
+    x = np.zeros((3, 96), np.uint16)
+    x[0, 32:64] = bf16(np.linspace(-1, 1, 32))
+    x[0, 40] = 0x7F80
+    x[0, 64:96] = bf16(np.linspace(-3, 3, 32))
+    x[0, 70] = 0xFFC1
+    x[0, 5] = 0x8000
+    x[1, :] = np.arange(96) + 1                      # BF16 subnormals only
+    x[2, :32] = 0x0001
+    x[2, 32:64] = bf16(np.full(32, 500.0))
+    x[2, 64:96] = bf16(np.full(32, -448.0))
+    q, s = mxq.mx_quantize_rowwise(to_dev_bf16(x))
+    rc, rs = mx.mx_quantize_rowwise(x)
+    assert np.array_equal(host(s), rs) and np.array_equal(host(q), rc)
+
+
+def test_rowwise_empty_is_noop():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s = mxq.mx_quantize_rowwise(x)
+    assert q.shape == (0, 64) and s.shape == (0, 2)
+
+
+# ---------------------------------------------------------------------------
+# column-wise
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(32, 16), (256, 96), (160, 1408), (96, 2064)])
+def test_colwise_plain(M, K):
+    say(f"colwise M={M} K={K}")
+    x = workloads.bf16_normal((M, K), 1.0, seed=K, name="cw", outlier_frac=0.01,
+                              outlier_scale=100.0)
+    qT, sT, _ = mxq.mx_quantize_colwise(to_dev_bf16(x))
+    rc, rs = mx.mx_quantize_colwise(x)
+    qh, sh = host(qT), host(sT)
+    assert np.array_equal(qh[:, :M], rc) and np.array_equal(sh[:, :M // 32], rs)
+    assert np.all(qh[:, M:] == 0) and np.all(sh[:, M // 32:] == 0)
+
+
+@pytest.mark.parametrize("counts", [
+    [40, 0, 1, 32, 0, 70, 0],
+    [0, 0, 0, 5],
+    [300],
+    [1] * 9 + [0] * 3 + [77],
+])
+def test_colwise_grouped(counts):
+    say(f"colwise grouped counts={counts}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    M, K = int(counts.sum()), 208
+    x = workloads.bf16_normal((M, K), 1e-3, seed=int(M), name="cg", outlier_frac=0.01,
+                              outlier_scale=30.0)
+    qT, sT, poff = mxq.mx_quantize_colwise(to_dev_bf16(x), to_dev(offs))
+    rc, rs, rpoff = mx.mx_quantize_grouped_colwise(x, offs)
+    Mp = int(rpoff[-1])
+    assert np.array_equal(host(poff), rpoff)
+    qh, sh = host(qT), host(sT)
+    assert np.array_equal(qh[:, :Mp], rc) and np.array_equal(sh[:, :Mp // 32], rs)
+    assert np.all(qh[:, Mp:] == 0) and np.all(sh[:, Mp // 32:] == 0)
+
+
+def test_colwise_grouped_moe_backward_sampled_columns():
+    """Full-size grouped column quant of dY [49152, 2048] with Zipf expert
+    counts; the oracle checks 48 sampled columns (columns are independent)."""
+    say("colwise grouped dY 49152x2048")
+    counts = workloads.moe_counts(0)
+    offs = workloads.offsets_from_counts(counts)
+    dY = workloads.moe_backward(0)["dY"]
+    qT, sT, poff = mxq.mx_quantize_colwise(to_dev_bf16(dY), to_dev(offs))
+    cols = np.random.default_rng(0).choice(dY.shape[1], 48, replace=False)
+    rc, rs, rpoff = mx.mx_quantize_grouped_colwise(np.ascontiguousarray(dY[:, cols]), offs)
+    Mp = int(rpoff[-1])
+    assert np.array_equal(host(poff), rpoff)
+    qh = host(qT[torch.from_numpy(cols).cuda()])
+    sh = host(sT[torch.from_numpy(cols).cuda()])
+    assert np.array_equal(qh[:, :Mp], rc) and np.array_equal(sh[:, :Mp // 32], rs)
+
+
+def test_colwise_matches_rowwise_of_transpose_on_gpu():
+    x = workloads.bf16_normal((128, 192), 1.0, seed=3, name="ct")
+    qT, sT, _ = mxq.mx_quantize_colwise(to_dev_bf16(x))
+    q2, s2 = mxq.mx_quantize_rowwise(to_dev_bf16(np.ascontiguousarray(x.T)))
+    assert torch.equal(qT[:, :128], q2) and torch.equal(sT[:, :4], s2)
+
+
+# ---------------------------------------------------------------------------
+# per-tensor
+# ---------------------------------------------------------------------------
+
+def _pt_check(bits):
+    q, s = mxq.fp8_quantize_per_tensor(to_dev_bf16(bits))
+    rc, rsc = per_tensor.pt_quantize(bits)
+    assert host(s)[0] == rsc
+    assert np.array_equal(host(q), rc)
+
+
+@pytest.mark.parametrize("amax", [448.0, 1.0, 3.0e-3, 7.7e5, 2.0 ** -100, 2.0 ** -125,
+                                  1.0e-37, 3.0e38])
+def test_per_tensor_all_patterns_below_amax(amax):
+    """Every finite BF16 pattern with |x| <= amax, plus amax itself."""
+    say(f"per-tensor all patterns amax={amax}")
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = codec.bf16_bits_to_f64(pats)
+    a = codec.bf16_bits_to_f64(bf16([amax]))[0]
+    keep = pats[np.isfinite(v) & (np.abs(v) <= a)]
+    bits = np.concatenate([bf16([amax, -amax]), keep])
+    _pt_check(bits)
+
+
+def test_per_tensor_workloads_full_size():
+    d = workloads.dense_ffn(0)
+    for name in ("X", "W"):
+        say(f"per-tensor dense FFN {name}")
+        _pt_check(d[name])
+
+
+@pytest.mark.parametrize("n", [1, 7, 9, 1023, 4099])
+def test_per_tensor_tails(n):
+    _pt_check(workloads.bf16_normal((n,), 0.5, seed=n, name="pt"))
+
+
+def test_per_tensor_nonfinite_and_zero():
+    _pt_check(np.array([0x3F80, 0x7FC0, 0xFF80, 0x7F80, 0xC000, 0xFFC0, 0x0001, 0x8000] * 3,
+                       np.uint16))
+    _pt_check(np.zeros(40, np.uint16))
+    _pt_check(np.full(24, 0x8000, np.uint16))
+
+
+def test_per_tensor_empty():
+    x = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    q, s = mxq.fp8_quantize_per_tensor(x)
+    assert host(s)[0] == 1.0
