@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE routed-expert layer step (forward, dgrad and wgrad) of a
+DeepSeek-V3 16B-shaped model with every operand MX-FP8 quantized on the fly,
+on one MI355X.
+
+Step (all on one HIP stream, inputs resident in HBM):
+  forward   X·W_guᵀ (64 experts, grouped by rows) and h·W_dnᵀ
+  dgrad     dY·W_dn and dGU·W_gu (weights column-quantized per expert)
+  wgrad     dW_dn[e] = dY_eᵀ·h_e and dW_gu[e] = dGU_eᵀ·X_e over each expert's
+            tokens (grouped column quantization, groups padded to 32)
+  quantization of X, h, dY, dGU (row and grouped-column copies) and of W_gu,
+  W_dn (row and column copies) every step.
+Synthetic inputs: 8192 tokens x top-6 = 49152 rows, expert counts drawn as a
+multinomial over Zipf(1.1) expert probabilities (seed 0); BF16 N(0,1)
+activations, N(0,0.02) weights, N(0,1e-3) gradients; h and dGU stand in for
+the SwiGLU output and its backward.
+
+Prints one JSON line: metric value = algorithmic GEMM FLOPs of the step
+divided by the step time (quantization included).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 grouped-GEMM TFLOP/s incl. quant (fwd+dgrad+wgrad); % MX-FP8 peak"
+PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense MX-FP8 (E4M3) matrix peak
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+MX_BYTES_PER_ELT = 2 + 1 + 1 / 32   # BF16 in, E4M3 code + E8M0 per 32 out
+HIDDEN, FFN, E, TOKENS, TOP_K = 2048, 1408, 64, 8192, 6
+
+# kernel-function names as rocprofv3 reports them
+KFN = {
+    "q_row": "k_mx_rowwise",
+    "q_col": "k_mx_colwise",
+    "gmm": "k_gemm<1,false,0>",
+    "wgrad": "k_gemm<2,false,0>",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
+    return ap.parse_args()
+
+
+class Timer:
+    """Per-label HIP event pairs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ev = {}
+        self.on = False
+
+    def run(self, label, fn, *a, **k):
+        if not self.on:
+            return fn(*a, **k)
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn(*a, **k)
+        e.record()
+        self.ev.setdefault(label, []).append((s, e))
+        return r
+
+    def ms(self):
+        return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.ev.items()}
+
+    def count(self):
+        return {k: len(v) for k, v in self.ev.items()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_quant_gemm_amd import mxq, workloads
+
+    mxq.load()                                   # fails loudly without the HIP library
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.bfloat16).to(dev)
+
+    # ---------------- inputs ----------------
+    fw = workloads.moe_forward(args.seed, TOKENS, TOP_K, E)
+    bw = workloads.moe_backward(args.seed, TOKENS, TOP_K, E)
+    counts, offs = fw["counts"], fw["offsets"]
+    M = int(counts.sum())
+    X, h = to_dev(fw["X"]), to_dev(fw["h"])
+    Wgu = to_dev(fw["W_gu"].reshape(E * 2 * FFN, HIDDEN))
+    Wdn = to_dev(fw["W_dn"].reshape(E * HIDDEN, FFN))
+    dY, dGU = to_dev(bw["dY"]), to_dev(bw["dGU"])
+    offs_d = torch.from_numpy(offs).to(dev)
+    w_off_gu = torch.arange(E + 1, dtype=torch.int64, device=dev) * (2 * FFN)
+    w_off_dn = torch.arange(E + 1, dtype=torch.int64, device=dev) * HIDDEN
+
+    T = Timer(torch)
+
+    def step():
+        # forward
+        xq, xs = T.run("q_row", mxq.mx_quantize_rowwise, X)
+        wq, ws = T.run("q_row", mxq.mx_quantize_rowwise, Wgu)
+        gu = T.run("gmm", mxq.mx_grouped_gemm, xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                   ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
+        hq, hs = T.run("q_row", mxq.mx_quantize_rowwise, h)
+        dq, dsc = T.run("q_row", mxq.mx_quantize_rowwise, Wdn)
+        y = T.run("gmm", mxq.mx_grouped_gemm, hq, hs, dq.view(E, HIDDEN, FFN),
+                  dsc.view(E, HIDDEN, FFN // 32), offs_d)
+        # dgrad
+        gq, gs = T.run("q_row", mxq.mx_quantize_rowwise, dY)
+        dnT, dnTs, _ = T.run("q_col", mxq.mx_quantize_colwise, Wdn, w_off_dn)
+        bq, bs = mxq.expert_view(dnT, dnTs, E, HIDDEN)          # [E, 1408, 2048]
+        dh = T.run("gmm", mxq.mx_grouped_gemm, gq, gs, bq, bs, offs_d)
+        uq, us = T.run("q_row", mxq.mx_quantize_rowwise, dGU)
+        guT, guTs, _ = T.run("q_col", mxq.mx_quantize_colwise, Wgu, w_off_gu)
+        bq2, bs2 = mxq.expert_view(guT, guTs, E, 2 * FFN)       # [E, 2048, 2816]
+        dx = T.run("gmm", mxq.mx_grouped_gemm, uq, us, bq2, bs2, offs_d)
+        # wgrad
+        dyT, dyTs, poff = T.run("q_col", mxq.mx_quantize_colwise, dY, offs_d)
+        hT, hTs, _ = T.run("q_col", mxq.mx_quantize_colwise, h, offs_d)
+        dwdn = T.run("wgrad", mxq.mx_grouped_gemm_wgrad, dyT, dyTs, hT, hTs, poff)
+        duT, duTs, _ = T.run("q_col", mxq.mx_quantize_colwise, dGU, offs_d)
+        xT, xTs, _ = T.run("q_col", mxq.mx_quantize_colwise, X, offs_d)
+        dwgu = T.run("wgrad", mxq.mx_grouped_gemm_wgrad, duT, duTs, xT, xTs, poff)
+        return gu, y, dh, dx, dwdn, dwgu
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    T.on = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    T.on = False
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---------------- algorithmic work ----------------
+    per_dir = 2 * M * (2 * FFN * HIDDEN + HIDDEN * FFN)       # fwd (= dgrad = wgrad) FLOPs
+    flops = 3 * per_dir
+    value = flops / (ms_step * 1e-3) / 1e12
+    quant_elts = {
+        "q_row": [M * HIDDEN, E * 2 * FFN * HIDDEN, M * FFN, E * HIDDEN * FFN, M * HIDDEN,
+                  M * 2 * FFN],
+        "q_col": [E * HIDDEN * FFN, E * 2 * FFN * HIDDEN, M * HIDDEN, M * FFN, M * 2 * FFN,
+                  M * HIDDEN],
+    }
+    gemm_flops = {
+        "gmm": [2 * M * 2 * FFN * HIDDEN, 2 * M * HIDDEN * FFN, 2 * M * FFN * HIDDEN,
+                2 * M * HIDDEN * 2 * FFN],
+        "wgrad": [2 * M * HIDDEN * FFN, 2 * M * 2 * FFN * HIDDEN],
+    }
+    avg_ms = T.ms()
+    n_launch = T.count()
+    per_step_ms = {k: avg_ms[k] * n_launch[k] / args.steps for k in avg_ms}
+    breakdown = {}
+    for k in ("q_row", "q_col"):
+        work = sum(quant_elts[k]) * MX_BYTES_PER_ELT
+        breakdown[KFN[k]] = {
+            "launches_per_step": n_launch[k] // args.steps, "ms_per_step": per_step_ms[k],
+            "avg_launch_us": avg_ms[k] * 1e3,
+            "GB_per_s": work / (per_step_ms[k] * 1e-3) / 1e9,
+            "frac_hbm_peak": work / (per_step_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    for k in ("gmm", "wgrad"):
+        work = sum(gemm_flops[k])
+        breakdown[KFN[k]] = {
+            "launches_per_step": n_launch[k] // args.steps, "ms_per_step": per_step_ms[k],
+            "avg_launch_us": avg_ms[k] * 1e3,
+            "TFLOP_per_s": work / (per_step_ms[k] * 1e-3) / 1e12,
+            "frac_mfma_peak": work / (per_step_ms[k] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS}
+    gemm_ms = per_step_ms["gmm"] + per_step_ms["wgrad"]
+    quant_ms = per_step_ms["q_row"] + per_step_ms["q_col"]
+    quant_bytes = (sum(quant_elts["q_row"]) + sum(quant_elts["q_col"])) * MX_BYTES_PER_ELT
+
+    dom = max(per_step_ms, key=per_step_ms.get)
+    if dom in gemm_flops:
+        per_launch = sum(gemm_flops[dom]) / len(gemm_flops[dom])
+        achieved = per_launch / (avg_ms[dom] * 1e-3) / 1e12
+        roof = {"kernel": KFN[dom], "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS}
+    else:
+        per_launch = sum(quant_elts[dom]) * MX_BYTES_PER_ELT / len(quant_elts[dom])
+        achieved = per_launch / (avg_ms[dom] * 1e-3) / 1e9
+        roof = {"kernel": KFN[dom], "bound": "hbm", "achieved": achieved,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS}
+    roof["traffic"] = measured_traffic(roof["kernel"])
+
+    components = {"moe_step": breakdown,
+                  "gemm_only_TFLOP_per_s": flops / (gemm_ms * 1e-3) / 1e12,
+                  "quant_only_GB_per_s": quant_bytes / (quant_ms * 1e-3) / 1e9,
+                  "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
+    if not args.no_dense:
+        components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(fw, bw, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8_e4m3", "data": "synthetic",
+        "config": {"workload": "moe_expert_layer_fwd_dgrad_wgrad", "tokens": TOKENS,
+                   "top_k": TOP_K, "rows": M, "experts": E, "hidden": HIDDEN,
+                   "moe_ffn": FFN, "expert_counts": "multinomial over Zipf(1.1), seed %d" % args.seed,
+                   "max_expert_rows": int(counts.max()), "min_expert_rows": int(counts.min()),
+                   "weights_quantized_each_step": True, "algorithmic_flops": flops},
+        "pct_mx_fp8_peak": 100.0 * value / PEAK_MFMA_TFLOPS,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "components": components,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        from block_quant_gemm_amd.build import source_digest
+        if rec.get("source_digest") != source_digest():
+            return None
+        k = rec.get("kernels", {}).get(kernel)
+        return None if k is None else k.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
+    """Dense FFN gate/up projection: X 8192x2048 (0.5% outliers x50), W
+    10944x2048: MX row quant of both and the forward GEMM; per-tensor E4M3
+    quant of both and the per-tensor GEMM."""
+    d = workloads.dense_ffn(seed)
+    X, W = to_dev(d["X"]), to_dev(d["W"])
+    nX, nW = X.numel(), W.numel()
+    flops = 2 * X.shape[0] * W.shape[0] * X.shape[1]
+
+    def timed(fn, *a):
+        for _ in range(2):
+            r = fn(*a)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            r = fn(*a)
+        e.record()
+        torch.cuda.synchronize()
+        return r, s.elapsed_time(e) / reps
+
+    (xq, xs), t_qx = timed(mxq.mx_quantize_rowwise, X)
+    (wq, ws), t_qw = timed(mxq.mx_quantize_rowwise, W)
+    _, t_g = timed(mxq.mx_gemm, xq, xs, wq, ws)
+    (px, sx), t_px = timed(mxq.fp8_quantize_per_tensor, X)
+    (pw, sw), t_pw = timed(mxq.fp8_quantize_per_tensor, W)
+    _, t_pg = timed(mxq.fp8_gemm_per_tensor, px, sx, pw, sw)
+    gb = lambda n, b, ms: n * b / (ms * 1e-3) / 1e9
+    return {
+        "shape": "X 8192x2048, W 10944x2048",
+        "mx_quant_X": {"us": t_qx * 1e3, "GB_per_s": gb(nX, MX_BYTES_PER_ELT, t_qx)},
+        "mx_quant_W": {"us": t_qw * 1e3, "GB_per_s": gb(nW, MX_BYTES_PER_ELT, t_qw)},
+        "mx_gemm_fwd": {"us": t_g * 1e3, "TFLOP_per_s": flops / (t_g * 1e-3) / 1e12},
+        "per_tensor_quant_X": {"us": t_px * 1e3, "GB_per_s_algorithmic": gb(nX, 3, t_px)},
+        "per_tensor_quant_W": {"us": t_pw * 1e3, "GB_per_s_algorithmic": gb(nW, 3, t_pw)},
+        "per_tensor_gemm_fwd": {"us": t_pg * 1e3, "TFLOP_per_s": flops / (t_pg * 1e-3) / 1e12},
+    }
+
+
+def cpu_baseline(fw, bw, budget_s):
+    """The CPU oracle (unchanged) on a bounded sample of the same step: whole
+    experts, smallest first, until about ``budget_s`` seconds of CPU time;
+    TFLOP/s = the sample's algorithmic GEMM FLOPs / oracle time."""
+    import numpy as np
+    from oracle import gemm, mx
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    counts, offs = fw["counts"], fw["offsets"]
+    order = np.argsort(counts, kind="stable")
+    done, flops, t_tot = [], 0, 0.0
+    for e in order:
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        t0 = time.perf_counter()
+        xq, xs = mx.mx_quantize_rowwise(fw["X"][lo:hi])
+        wq, ws = mx.mx_quantize_rowwise(fw["W_gu"][e])
+        gemm.gemm_ref(mx.mx_dequantize(xq, xs), mx.mx_dequantize(wq, ws))
+        hq, hs = mx.mx_quantize_rowwise(fw["h"][lo:hi])
+        dq, dsc = mx.mx_quantize_rowwise(fw["W_dn"][e])
+        gemm.gemm_ref(mx.mx_dequantize(hq, hs), mx.mx_dequantize(dq, dsc))
+        gq, gs = mx.mx_quantize_rowwise(bw["dY"][lo:hi])
+        bq, bs = mx.mx_quantize_colwise(fw["W_dn"][e])
+        gemm.gemm_ref(mx.mx_dequantize(gq, gs), mx.mx_dequantize(bq, bs))
+        uq, us = mx.mx_quantize_rowwise(bw["dGU"][lo:hi])
+        bq2, bs2 = mx.mx_quantize_colwise(fw["W_gu"][e])
+        gemm.gemm_ref(mx.mx_dequantize(uq, us), mx.mx_dequantize(bq2, bs2))
+        one = np.array([0, hi - lo], np.int64)
+        aT, aTs, p = mx.mx_quantize_grouped_colwise(bw["dY"][lo:hi], one)
+        bT, bTs, _ = mx.mx_quantize_grouped_colwise(fw["h"][lo:hi], one)
+        gemm.grouped_wgrad_ref(mx.mx_dequantize(aT, aTs), mx.mx_dequantize(bT, bTs), p)
+        aT, aTs, p = mx.mx_quantize_grouped_colwise(bw["dGU"][lo:hi], one)
+        bT, bTs, _ = mx.mx_quantize_grouped_colwise(fw["X"][lo:hi], one)
+        gemm.grouped_wgrad_ref(mx.mx_dequantize(aT, aTs), mx.mx_dequantize(bT, bTs), p)
+        t_tot += time.perf_counter() - t0
+        flops += 6 * (hi - lo) * (2 * FFN * HIDDEN + HIDDEN * FFN)
+        done.append(int(e))
+        if t_tot >= budget_s:
+            break
+    return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "host_cpus": os.cpu_count(),
+            "sample": "full fwd+dgrad+wgrad oracle path (quant, dequant, FP64 GEMM and "
+                      "|A|·|B| magnitudes) for %d whole experts, smallest first (%d rows); "
+                      "%.1f s" % (len(done), sum(int(counts[e]) for e in done), t_tot)}
+
+
+if __name__ == "__main__":
+    main()

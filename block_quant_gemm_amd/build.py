@@ -10,6 +10,18 @@ SOURCES = ["csrc/quant.hip", "csrc/gemm.hip", "csrc/api.hip"]
 LIB = os.path.join(PKG, "libmxq.so")
 
 
+def source_digest():
+    """SHA-256 of the kernel sources and the C header (identifies a build)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SOURCES + ["csrc/common.h"]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "include", "mxq.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.sep not in c or os.path.exists(c)):

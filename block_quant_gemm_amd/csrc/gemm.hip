@@ -138,6 +138,7 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t m, int64_t 
 struct GemmArgs {
   const uint8_t* a; const uint8_t* as; int64_t lda, ldsa;
   const uint8_t* b; const uint8_t* bs; int64_t ldb, ldsb;
+  int64_t b_estride, bs_estride;                    // per-group B strides (variable M)
   const float* pta; const float* ptb;               // per-tensor scales
   const int64_t* offsets; int32_t E;
   int64_t M, N, K;
@@ -216,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     m0 = s_off[e] + (int64_t)(tm - s_start[e]) * BM;
     const int64_t rows = s_off[e + 1] - m0;
     A = {g.a + m0 * g.lda, g.as + m0 * g.ldsa, g.lda, g.ldsa, rows};
-    const uint8_t* be = g.b + (int64_t)e * g.N * g.ldb;
-    const uint8_t* bse = g.bs + (int64_t)e * g.N * g.ldsb;
+    const uint8_t* be = g.b + (int64_t)e * g.b_estride;
+    const uint8_t* bse = g.bs + (int64_t)e * g.bs_estride;
     B = {be + n0 * g.ldb, bse + n0 * g.ldsb, g.ldb, g.ldsb, g.N - n0};
     c_row0 = m0; c_rows = rows;
   } else {
@@ -359,7 +360,7 @@ extern "C" int mx_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, in
     if ((st = check_operand(b, b_scale, ldb, ldsb, K, true))) return st;
   }
   if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;   // exact-product mode: not built yet
-  GemmArgs g{a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, nullptr, nullptr, nullptr, 0,
+  GemmArgs g{a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, 0, 0, nullptr, nullptr, nullptr, 0,
              M, N, K, c, ldc, (uint32_t)((N + BN - 1) / BN)};
   const int64_t blocks = ((M + BM - 1) / BM) * (int64_t)g.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
@@ -380,7 +381,7 @@ extern "C" int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64
     if ((st = check_operand(b, b_scale, ldb, 0, K, false))) return st;
   }
   if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
-  GemmArgs g{a, nullptr, lda, 0, b, nullptr, ldb, 0, a_scale, b_scale, nullptr, 0,
+  GemmArgs g{a, nullptr, lda, 0, b, nullptr, ldb, 0, 0, 0, a_scale, b_scale, nullptr, 0,
              M, N, K, c, ldc, (uint32_t)((N + BN - 1) / BN)};
   const int64_t blocks = ((M + BM - 1) / BM) * (int64_t)g.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
@@ -389,6 +390,7 @@ extern "C" int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64
 
 extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, int64_t ldsa,
                                const uint8_t* b, const uint8_t* b_scale, int64_t ldb, int64_t ldsb,
+                               int64_t b_estride, int64_t bs_estride,
                                const int64_t* offsets, int32_t E, int64_t M, int64_t N, int64_t K,
                                void* c, int64_t ldc, int out_dtype, int accum,
                                hipStream_t stream) {
@@ -403,9 +405,11 @@ extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t
     if ((st = check_operand(a, a_scale, lda, ldsa, K, true))) return st;
     if ((st = check_operand(b, b_scale, ldb, ldsb, K, true))) return st;
   }
+  if (b_estride < 0 || bs_estride < 0) return MXQ_ERR_SHAPE;
+  if (b_estride % 16 != 0) return MXQ_ERR_ALIGN;
   if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
-  GemmArgs g{a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, nullptr, nullptr, offsets, E,
-             M, N, K, c, ldc, (uint32_t)((N + BN - 1) / BN)};
+  GemmArgs g{a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, b_estride, bs_estride, nullptr,
+             nullptr, offsets, E, M, N, K, c, ldc, (uint32_t)((N + BN - 1) / BN)};
   const int64_t mtiles = (M + BM - 1) / BM + E;      // upper bound over all group splits
   const int64_t blocks = mtiles * (int64_t)g.tiles_n;
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
@@ -430,7 +434,7 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale,
   int64_t scap = (ldsa_t < ldsb_t ? ldsa_t : ldsb_t) * 32;
   if (scap < cap) cap = scap;
   if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
-  GemmArgs g{at, at_scale, lda_t, ldsa_t, bt, bt_scale, ldb_t, ldsb_t, nullptr, nullptr,
+  GemmArgs g{at, at_scale, lda_t, ldsa_t, bt, bt_scale, ldb_t, ldsb_t, 0, 0, nullptr, nullptr,
              offsets_padded, E, N, K, cap, c, ldc, (uint32_t)((K + BN - 1) / BN)};
   // GemmArgs fields for this kind: M = N (rows of dW), N = K (cols of dW), K = token capacity.
   g.M = N; g.N = K; g.K = cap;

@@ -32,7 +32,7 @@ _SIGS = {
                                _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
     "fp8_gemm_per_tensor": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
                                            _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
-    "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p, _i32,
+    "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _i32,
                                        _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                        ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p,
@@ -198,16 +198,30 @@ def mx_grouped_gemm(a, a_scale, b, b_scale, offsets, out_dtype=OUT_BF16,
                     accum=ACC_MFMA_FP8, c=None):
     """Variable-M grouped GEMM: rows [o_e, o_e+1) of A times B[e]ᵀ.
 
-    a [M, K], b [E, N, K] codes with scales [M, K/32], [E, N, K/32];
+    a [M, K] codes with scales [M, K/32]; b [E, N, K] codes with scales
+    [E, N, K/32], any strides (e.g. a view of column-quantized weights);
     offsets int64 [E+1] on the device."""
     M, K = a.shape
     E, N, _ = b.shape
     c = _out(M, N, out_dtype, a.device, c)
     _check(load().mx_grouped_gemm(_ptr(a), _ptr(a_scale), a.stride(0), a_scale.stride(0),
                                   _ptr(b), _ptr(b_scale), b.stride(1), b_scale.stride(1),
-                                  _ptr(offsets), E, M, N, K, _ptr(c), c.stride(0),
-                                  out_dtype, accum, _stream()))
+                                  b.stride(0), b_scale.stride(0), _ptr(offsets), E, M, N, K,
+                                  _ptr(c), c.stride(0), out_dtype, accum, _stream()))
     return c
+
+
+def expert_view(qT, sT, E, rows_per_expert):
+    """[E, K, rows_per_expert] strided views of column-quantized weights.
+
+    mx_quantize_colwise of a weight stack [E*R, K] with one group per expert
+    (R rows each, R % 32 == 0) returns codes [K, E*R]; expert e's transposed
+    weight is the column slice [:, e*R:(e+1)*R]."""
+    K = qT.shape[0]
+    R = rows_per_expert
+    q = qT.as_strided((E, K, R), (R, qT.stride(0), 1))
+    s = sT.as_strided((E, K, R // 32), (R // 32, sT.stride(0), 1))
+    return q, s
 
 
 def mx_grouped_gemm_wgrad(at, at_scale, bt, bt_scale, offsets_padded, out_dtype=OUT_BF16,

@@ -182,15 +182,21 @@ MXQ_API int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64_t 
  *   For each group e with rows [offsets[e], offsets[e+1]):
  *     C[rows, :] = A[rows, :] · B_eᵀ
  *   a, a_scale  : device, [M, K] codes / [M, K/32] scales, row strides lda, ldsa.
- *   b, b_scale  : device, [E, N, K] codes / [E, N, K/32] scales, expert e at
- *                 b + e*N*ldb and b_scale + e*N*ldsb.
+ *   b, b_scale  : device, per expert e an [N, K] code matrix at
+ *                 b + e*b_estride (row stride ldb) and its [N, K/32] scales at
+ *                 b_scale + e*bs_estride (row stride ldsb).  A contiguous
+ *                 [E, N, K] tensor has b_estride = N*ldb, bs_estride = N*ldsb;
+ *                 the column-quantized weights of mx_quantize_colwise (one
+ *                 group per expert) have b_estride = rows per expert and
+ *                 bs_estride = rows per expert / 32.
  *   offsets     : device int64 [E+1], as for mx_quantize_colwise.
  *   c           : device [M, N], row stride ldc.
  * Rows of empty groups do not exist; nothing else is written.
- * Same alignment requirements as mx_gemm.
+ * Same alignment requirements as mx_gemm; b_estride % 16 == 0.
  */
 MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, int64_t ldsa,
                     const uint8_t* b, const uint8_t* b_scale, int64_t ldb, int64_t ldsb,
+                    int64_t b_estride, int64_t bs_estride,
                     const int64_t* offsets, int32_t E,
                     int64_t M, int64_t N, int64_t K,
                     void* c, int64_t ldc, int out_dtype, int accum,

@@ -56,8 +56,9 @@ def test_host_validation_errors(lib):
     assert lib.mx_gemm(P, P, 32, 1, P, P, 32, 1, 4, 8, 32, P, 4, 0, 0, None) == 2  # ldc < N
     assert lib.mx_gemm(P, P, 24, 1, P, P, 32, 1, 4, 4, 32, P, 4, 0, 0, None) == 2  # lda < K
     assert lib.mx_gemm(None, None, 32, 1, None, None, 32, 1, 0, 4, 32, None, 4, 0, 0, None) == 0
-    assert lib.mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, None, 4, 8, 8, 32, P, 8, 0, 0, None) == 1
-    assert lib.mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, P, 0, 8, 8, 32, P, 8, 0, 0, None) == 2
+    assert lib.mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, 256, 8, None, 4, 8, 8, 32, P, 8, 0, 0, None) == 1
+    assert lib.mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, 256, 8, P, 0, 8, 8, 32, P, 8, 0, 0, None) == 2
+    assert lib.mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, 250, 8, P, 4, 8, 8, 32, P, 8, 0, 0, None) == 3
     assert lib.mx_grouped_gemm_wgrad(P, P, 40, 2, P, P, 32, 1, P, 2, 8, 8, P, 8, 0, 0, None) == 3
     assert lib.fp8_quantize_per_tensor(P, -5, P, P, P, 4096, None) == 2
     assert lib.fp8_quantize_per_tensor(P, 100, P, P, P, 4, None) == 5          # workspace
