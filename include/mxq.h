@@ -154,8 +154,9 @@ typedef enum { MXQ_ACC_MFMA_FP8 = 0, MXQ_ACC_FP32 = 1 } mxq_accum;
  *   a_scale, b_scale : device E8M0 [M, K/32] / [N, K/32], row strides
  *                  ldsa, ldsb bytes (>= K/32).
  *   c            : device output [M, N], row stride ldc elements, BF16 or FP32.
- * Requires K % 32 == 0; lda, ldb % 16 == 0; a, b 16-byte aligned;
- * ldsa, ldsb % 4 == 0 and scale pointers 4-byte aligned; ldc >= N.
+ * Requires K % 32 == 0; lda, ldb % 16 == 0; a, b 16-byte aligned; ldc >= N;
+ * (M rows of lda bytes and the scale rows) addressable with 32-bit offsets
+ * per 256-row tile.  Scale pointers and strides have no alignment rule.
  * K == 0 writes zeros; M == 0 or N == 0 is a no-op.
  */
 MXQ_API int mx_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, int64_t ldsa,
@@ -214,8 +215,7 @@ MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t ld
  *   For each group e: dW_e[N, K] = Σ_{t in [poff[e], poff[e+1])} at[:, t] · bt[:, t]ᵀ
  *   c : device [E, N, K] with row stride ldc and expert stride N*ldc; an empty
  *       group writes zeros.
- * Requires lda_t, ldb_t % 16 == 0, ldsa_t, ldsb_t % 4 == 0, 16-byte aligned
- * code pointers, 4-byte aligned scale pointers.
+ * Requires lda_t, ldb_t % 16 == 0 and 16-byte aligned code pointers.
  */
 MXQ_API int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t, int64_t ldsa_t,
                           const uint8_t* bt, const uint8_t* bt_scale, int64_t ldb_t, int64_t ldsb_t,
