@@ -28,15 +28,30 @@
 #include "common.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace mxq {
 
-constexpr int TM = 256, TN = 256, TK = 64;
-constexpr int kThreads = 256;
-constexpr int kStages = 4;                        // LDS ring: 3 steps in flight
-constexpr int kStage = TM * TK;                   // bytes per operand per stage (16 KB)
+constexpr int TM = 256, TN = 256;
+constexpr int TK = 64;                            // k-step: one MFMA deep
+constexpr int TS = 128;                           // stage: two k-steps, 128-byte row segments
+constexpr int kThreads = 512;                     // 8 wavefronts, 2 per SIMD
+constexpr int kSlots = 2;                         // LDS ring of stages
+constexpr int kStage = TM * TS;                   // bytes per operand per stage (32 KB)
 constexpr int kGroupM = 4;                        // M tiles per rasterization group
 constexpr int kMaxGroups = 256;
+
+// Compile-time loops: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, B + I>{}), ...);
+}
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for_range(F&& f) {
+  static_for_seq<B>(f, std::make_integer_sequence<int, E - B>{});
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_range<0, N>(f); }
 
 enum GemmKind { kDense = 0, kVarM = 1, kVarK = 2 };
 
@@ -68,12 +83,12 @@ __device__ __forceinline__ i32x4 uniform(i32x4 r) {
 }
 __device__ __forceinline__ void dma_b128(i32x4 r, uint32_t m0, uint32_t off) {
   const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(off), "s"(r) : "memory");
 }
 __device__ __forceinline__ void dma_b8(i32x4 r, uint32_t m0, uint32_t off) {
   const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
                :: "s"(m), "v"(off), "s"(r) : "memory");
 }
 
@@ -81,11 +96,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
-// LDS offset of 16-byte chunk c (0..3) of tile row r: rows are 64 B; chunks
-// are XOR-swizzled with bits 1-2 of the row so 8 consecutive rows read at one
-// chunk index cover all 8 16-byte slots of a 128-byte bank line.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
-__device__ __forceinline__ int lds_off(int r, int c) { return r * TK + ((c ^ swz(r)) << 4); }
+// LDS offset of 16-byte chunk c (0..7) of tile row r in a stage: rows are
+// 128 B; chunks are XOR-swizzled with bits 1-3 of the row, so 16 consecutive
+// rows read at one chunk index (the 16 lanes the LDS serves per clock for
+// 16-byte reads) cover all 16 16-byte slots of the 256-byte bank line.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * TS + ((c ^ swz(r)) << 4); }
 
 struct GemmArgs {
   const uint8_t* a; const uint8_t* as; int64_t lda, ldsa;
@@ -104,13 +120,18 @@ struct GemmArgs {
 struct OpTile {
   i32x4 q, s;
   uint32_t ld, lds;
-  uint32_t smis;                                    // scale base misalignment (0..3)
+  uint32_t smis;                                    // scale base misalignment (0..3 bytes
+                                                    // or, for scale windows, 0..15)
   int rows;                                         // valid rows in this tile (<= 256)
 };
 
+// `windows`: scales are read in 16-byte windows (row strides are multiples of
+// 16, so every row has the same misalignment); the descriptor starts at the
+// 16-byte boundary at or below the tile's first scale and its range is rounded
+// up to whole windows, which never crosses a page the valid bytes are not in.
 __device__ __forceinline__ OpTile op_tile(const uint8_t* q, const uint8_t* s, int64_t ld,
                                           int64_t lds, int64_t row0, int64_t k0, int64_t rows,
-                                          int64_t kdim, bool scales) {
+                                          int64_t kdim, bool scales, bool windows) {
   OpTile t;
   const int r = rows > TM ? TM : (rows < 0 ? 0 : (int)rows);
   t.rows = r;
@@ -123,10 +144,12 @@ __device__ __forceinline__ OpTile op_tile(const uint8_t* q, const uint8_t* s, in
   if (scales) {
     const uint8_t* sb = s + row0 * lds + (k0 >> 5);
     const uintptr_t a = reinterpret_cast<uintptr_t>(sb);
-    t.smis = (uint32_t)(a & 3);
-    const uint8_t* sb4 = reinterpret_cast<const uint8_t*>(a & ~(uintptr_t)3);
-    const uint32_t sbytes = r > 0 ? (uint32_t)((r - 1) * lds + t.smis + ((kdim + 31) >> 5)) : 0;
-    t.s = make_rsrc(sb4, sbytes);
+    const uintptr_t align = windows ? 15 : 3;
+    t.smis = (uint32_t)(a & align);
+    const uint8_t* sba = reinterpret_cast<const uint8_t*>(a & ~align);
+    uint32_t sbytes = r > 0 ? (uint32_t)((r - 1) * lds + t.smis + ((kdim + 31) >> 5)) : 0;
+    if (windows) sbytes = (sbytes + 15) & ~15u;
+    t.s = make_rsrc(sba, sbytes);
   } else {
     t.smis = 0;
     t.s = t.q;
@@ -135,72 +158,41 @@ __device__ __forceinline__ OpTile op_tile(const uint8_t* q, const uint8_t* s, in
 }
 
 // Per-lane load offsets of one operand, computed once per workgroup.
-// Tile codes: wavefront w fills row groups g = 4w .. 4w+3 of the LDS slot
-// (16 rows, 1 KB each); lane i lands at byte 16 i of the group, i.e. row i/4
-// and slot i%4, which must hold chunk (i%4) ^ swz(row) under the swizzle.
-// Scales: entry e = 128 w + 64 k + i (k = 0, 1) of the slot's 512 scale
-// entries is block e%2 of the step for tile row e/2.
+// Codes: wavefront w fills row groups g = 4w .. 4w+3 (8 rows of 128 B, 1 KB
+// each) of the operand's LDS stage slot; lane i lands at byte 16 i of a
+// group, i.e. row i/8 and 16-byte slot i%8, which must hold chunk
+// (i%8) ^ swz(row); swz(8g + i/8) = 4 (g%2) + i/16, so the chunk depends on
+// the lane and the parity of j.
+// Scales (byte path): entry e = 64 w + i of the operand's 512 scale entries
+// per k-step is block e%2 of the step for tile row e/2.
 struct LaneOffsets {
   uint32_t q[4];            // row * ld + chunk * 16 (0x80000000 for rows past the tile)
-  uint32_t kchunk;          // chunk * 16 (the same for the lane's four rows)
-  uint32_t s[2];            // smis + row * lds + blk of scale entries k = 0, 1
+  uint32_t kc0;             // chunk * 16 for even j (odd j: kc0 ^ 64)
+  uint32_t s;               // smis + row * lds + blk of the lane's scale entry
+  uint32_t sblk;            // blk (0 or 1) of the lane's scale entry
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets(const OpTile& t) {
   LaneOffsets o;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rsub = lane >> 2, slot = lane & 3;
-  const int chunk = slot ^ swz(rsub);             // swz(16 g + rsub) == swz(rsub)
-  o.kchunk = (uint32_t)(chunk * 16);
+  const int rsub = lane >> 3, slot = lane & 7;
+  o.kc0 = (uint32_t)((slot ^ (rsub >> 1)) * 16);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (w * 4 + j) * 16 + rsub;
-    o.q[j] = row < t.rows ? (uint32_t)(row * t.ld) + o.kchunk : 0x80000000u;
+    const int row = (w * 4 + j) * 8 + rsub;
+    const uint32_t kc = o.kc0 ^ ((j & 1) * 64);     // == ((slot ^ swz(row)) * 16)
+    o.q[j] = row < t.rows ? (uint32_t)(row * t.ld) + kc : 0x80000000u;
   }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int e = w * 128 + k * 64 + lane;
-    o.s[k] = t.smis + (uint32_t)((e >> 1) * t.lds) + (uint32_t)(e & 1);
-  }
+  const int e = w * 64 + lane;
+  o.s = t.smis + (uint32_t)((e >> 1) * t.lds) + (uint32_t)(e & 1);
+  o.sblk = (uint32_t)(e & 1);
   return o;
 }
 
-// Issue the loads of one k-step of one operand: its 256 x 64 codes into an
-// LDS tile slot and, for MX, its 256 x 2 scale bytes into an LDS scale slot.
-// `q`, `sr` are the operand's descriptors or zero-range ones for steps past
-// the end.  Always 4 (+2) load instructions per wavefront.
-template <bool SCALES>
-__device__ __forceinline__ void issue_op(const LaneOffsets& o, i32x4 q, i32x4 sr,
-                                         uint8_t* tile_slot, uint32_t* scale_slot, int64_t step,
-                                         int64_t kdim) {
-  const int w = threadIdx.x >> 6;
-  const uint32_t kbyte = (uint32_t)(step * TK);
-  const bool tail = (int64_t)kbyte + TK > kdim;                  // uniform
-  const bool chunk_in = (int64_t)(kbyte + o.kchunk) < kdim;
-  const uint32_t tbase = lds_addr(tile_slot) + w * 4 * 1024;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t off = o.q[j] + kbyte;
-    if (tail && !chunk_in) off = 0x80000000u;
-    dma_b128(q, tbase + j * 1024, off);
-  }
-  if (SCALES) {
-    const uint32_t sbase = lds_addr(scale_slot) + w * 128 * 4;
-    const uint32_t kb2 = (uint32_t)(2 * step);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) dma_b8(sr, sbase + k * 256, o.s[k] + kb2);
-  }
-}
-
-// Blocks past the end of the contraction range hold zero codes; they get a
-// finite scale (2^0) so that 0 * scale cannot become NaN.
-__device__ __forceinline__ uint32_t scale_at(uint32_t raw, int64_t step, int half, int64_t kdim) {
-  return ((2 * step + half) << 5) < kdim ? raw : 127u;
-}
-
-__device__ __forceinline__ i32x8 read_frag(const uint8_t* l, int r, int half) {
-  const uint4 x = *reinterpret_cast<const uint4*>(l + lds_off(r, half));
-  const uint4 y = *reinterpret_cast<const uint4*>(l + lds_off(r, half + 2));
+// The MFMA operand of tile row r for one k-step: 16-byte chunks c0 and c1.
+__device__ __forceinline__ i32x8 read_frag(const uint8_t* l, int r, int c0, int c1) {
+  const uint4 x = *reinterpret_cast<const uint4*>(l + lds_off(r, c0));
+  const uint4 y = *reinterpret_cast<const uint4*>(l + lds_off(r, c1));
   i32x8 f;
   f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
   f[4] = y.x; f[5] = y.y; f[6] = y.z; f[7] = y.w;
@@ -293,10 +285,10 @@ __device__ void group_table(const int64_t* offsets, int E, int64_t M, int64_t* s
   __syncthreads();
 }
 
-// Vector-memory instructions a wavefront issues per k-step: 4 + 4 tile
-// loads, plus 2 + 2 scale-byte loads for MX.
-template <bool PT>
-constexpr int vmem_per_step() { return PT ? 8 : 12; }
+// Vector-memory instructions a wavefront issues per stage: 4 + 4 tile loads,
+// plus 2 + 2 scale-byte loads for MX scales read byte by byte.
+template <bool SBYTES>
+constexpr int vmem_per_stage() { return SBYTES ? 12 : 8; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -306,16 +298,34 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int KIND, bool PT, int OUT>
+// Scale windows: 3-slot ring of [A, B][256 rows][16 bytes] (16 blocks of 32,
+// i.e. 8 k-steps, per row).
+constexpr int kWinSlots = 3;
+constexpr int kWinBytes = 2 * TM * 16;
+
+// SW: MX scales read in 16-byte windows (row strides multiples of 16);
+// otherwise byte by byte (any stride).  PT: per-tensor scaled (no block scales).
+template <int KIND, bool PT, int OUT, bool SW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStage];  // [slot][A, B]
-  __shared__ uint32_t ssc[PT ? 1 : kStages * 2 * 2 * TM];           // [slot][A, B][row][blk]
+  constexpr bool SBYTES = !PT && !SW;               // per-step scale-byte loads
+  constexpr bool SWIN = !PT && SW;                  // scale windows
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * 2 * kStage];  // [slot][A, B]
+  // byte path: [slot][k-step][A, B][row][blk] as dwords;
+  // windows: [wslot][A, B][row][16 B]
+  __shared__ __attribute__((aligned(16)))
+  uint32_t ssc[SBYTES ? kSlots * 2 * 2 * 2 * TM : (SWIN ? kWinSlots * kWinBytes / 4 : 1)];
   __shared__ int64_t s_off[KIND == kVarM ? kMaxGroups + 1 : 1];
   __shared__ int32_t s_start[KIND == kVarM ? kMaxGroups + 1 : 1];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
+  // Wavefronts w and w + 4 share a SIMD.  Group grp = w / 4 owns output
+  // columns [128 grp, 128 grp + 128) of the tile; within it wavefront w
+  // computes rows [128 wm, +128) x columns [bn, bn + 64).
+  const int grp = wave >> 2, qw = wave & 3;
+  const int wm = qw >> 1;
+  const int bn = grp * 128 + (qw & 1) * 64;
   const int r32 = lane & 31, half = lane >> 5;
 
   // ---- map the workgroup to (group, m0, n0) ----
@@ -329,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     m0 = (int64_t)tm * TM;
     n0 = (int64_t)tn * TN;
     c_rows = g.M - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT);
-    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT);
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
+    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
   } else if (KIND == kVarM) {
     group_table(g.offsets, g.E, g.M, s_off, s_start);
     const uint32_t tiles_m = (uint32_t)s_start[g.E];  // data-dependent M-tile count
@@ -347,9 +357,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     m0 = s_off[e] + (int64_t)(tm - s_start[e]) * TM;
     n0 = (int64_t)tn * TN;
     c_rows = s_off[e + 1] - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, true);
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, true, SW);
     B = op_tile(g.b + (int64_t)e * g.b_estride, g.bs + (int64_t)e * g.bs_estride, g.ldb, g.ldsb,
-                n0, 0, g.N - n0, kdim, true);
+                n0, 0, g.N - n0, kdim, true, SW);
   } else {
     // variable K: tile = (e, tm over rows of A = dW rows, tn over rows of B =
     // dW cols).  Work per tile is proportional to the group's tokens, so the
@@ -367,107 +377,235 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     if (hi_t > (g.K & ~31LL)) hi_t = g.K & ~31LL;     // g.K holds the token capacity
     kdim = hi_t > lo_t ? hi_t - lo_t : 0;
     c_rows = g.M - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, lo_t, c_rows, kdim, true);
-    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, lo_t, g.N - n0, kdim, true);
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, lo_t, c_rows, kdim, true, SW);
+    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, lo_t, g.N - n0, kdim, true, SW);
     cbase = static_cast<uint8_t*>(g.c) + (int64_t)e * g.M * g.ldc * (OUT == MXQ_OUT_FP32 ? 4 : 2);
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int64_t nsteps = (kdim + TK - 1) / TK;
+  // kdim < 2^31 (the launchers check that a tile's byte offsets fit in 32 bits)
+  const uint32_t kdim32 = (uint32_t)kdim;
+  const int32_t nsteps = (int32_t)((kdim + TK - 1) / TK);
   const LaneOffsets oA = lane_offsets(A);
   const LaneOffsets oB = lane_offsets(B);
   const i32x4 none = make_rsrc(g.c, 0);              // zero range: loads read 0
+  const uint32_t lds_codes = lds_addr(smem), lds_scales = lds_addr(ssc);
 
-  // Issue the loads of k-step `step` into ring slot SLOT.  Steps past the end
-  // are issued too, through the zero-range descriptor, so each step always
-  // issues vmem_per_step<PT>() instructions per wavefront and the wait
-  // thresholds below are constants.
-  auto issue = [&](int64_t step, auto slot_tag) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    uint8_t* base = smem + SLOT * 2 * kStage;
-    uint32_t* sbase = ssc + (PT ? 0 : SLOT * 2 * 2 * TM);
-    const bool live = step < nsteps;
-    issue_op<!PT>(oA, uniform(live ? A.q : none), uniform(live ? A.s : none), base, sbase, step,
-                  kdim);
-    issue_op<!PT>(oB, uniform(live ? B.q : none), uniform(live ? B.s : none), base + kStage,
-                  sbase + 2 * TM, step, kdim);
+  const int32_t nstages = (nsteps + 1) / 2;
+  // This wavefront's share of the loads of stage u (k-steps 2u, 2u+1) into
+  // ring slot u % kSlots.  Dead stages load through the zero-range
+  // descriptor.  Only the last stage can be partial: its chunks and scale
+  // blocks past kdim load nothing (zero codes, scale code 0 = 2^-127,
+  // finite), so they add exact zeros.
+  // Code load d (0..7) of this wavefront's share of stage u: row group j = d/2
+  // of operand d%2.
+  auto stage_dma = [&](int32_t u, int d) {
+    const bool live = u < nstages;
+    const int j = d >> 1, op = d & 1;
+    const i32x4 q = uniform(live ? (op ? B.q : A.q) : none);
+    const uint32_t kb = (uint32_t)u * TS;
+    const uint32_t slot = (uint32_t)(u & (kSlots - 1));
+    const uint32_t kc = oA.kc0 ^ ((j & 1) * 64);
+    uint32_t off = kb + kc < kdim32 ? (op ? oB.q[j] : oA.q[j]) + kb : 0x80000000u;
+    asm volatile("" : "+v"(off));                   // select the offset, not the load
+    dma_b128(q, lds_codes + (slot * 2 + op) * kStage + wave * 4 * 1024 + j * 1024, off);
   };
-  auto compute = [&](int64_t step, auto slot_tag) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    const uint8_t* lA = smem + SLOT * 2 * kStage;
-    const uint8_t* lB = lA + kStage;
-    i32x8 fa[4], fb[4];
+  auto issue_stage_scales = [&](int32_t u) {
+    const bool live = u < nstages;
+    const uint32_t slot = (uint32_t)(u & (kSlots - 1));
+    if (SBYTES) {
+      const i32x4 sa = uniform(live ? A.s : none), sb = uniform(live ? B.s : none);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = read_frag(lA, wm * 128 + i * 32 + r32, half);
-      fb[i] = read_frag(lB, wn * 128 + i * 32 + r32, half);
-    }
-    uint32_t csa[4], csb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (PT) {
-        csa[i] = csb[i] = 127u;
-      } else {
-        const uint32_t* sA = ssc + SLOT * 2 * 2 * TM;
-        const uint32_t* sB = sA + 2 * TM;
-        csa[i] = scale_at(sA[(wm * 128 + i * 32 + r32) * 2 + half], step, half, kdim);
-        csb[i] = scale_at(sB[(wn * 128 + i * 32 + r32) * 2 + half], step, half, kdim);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint32_t st = 2 * (uint32_t)u + ks;
+        uint32_t soff = (2 * st + oA.sblk) * 32 < kdim32 ? 2 * st : 0x80000000u;
+        asm volatile("" : "+v"(soff));
+        const uint32_t sbase = lds_scales + (slot * 2 + ks) * 2 * 2 * TM * 4 + wave * 64 * 4;
+        dma_b8(sa, sbase, oA.s + soff);
+        dma_b8(sb, sbase + 2 * TM * 4, oB.s + soff);
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fb[j], fa[i], acc[i][j], 0, 0, 0, (int)csb[j], 0, (int)csa[i]);
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  static_assert(kStages == 4, "the unrolled ring below assumes 4 slots");
+  auto issue_stage = [&](int32_t u) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) stage_dma(u, d);
+    issue_stage_scales(u);
+  };
+  // Scale windows: wavefront w loads rows [64 (w%4), +64) of operand w/4;
+  // window j of a row holds its scale bytes [16 j - smis, 16 j + 16 - smis)
+  // of the contraction range, in ring slot j % kWinSlots.  Steps 8p .. 8p+7
+  // read windows p and p+1; window p+2 is loaded during step 8p+1, into the
+  // slot of window p-1.
+  const uint32_t lds_win = lds_scales;
+  const int wop = wave >> 2;
+  const uint32_t win_off = (uint32_t)(((wave & 3) * 64 + lane) * (wop ? B.lds : A.lds));
+  const uint32_t nblk = (kdim32 + 31) >> 5;
+  // Only windows holding a block of the range are loaded (the others go
+  // through the zero-range descriptor): with an empty range the scale
+  // pointers may be null.
+  auto issue_window = [&](int32_t j) {
+    const bool live = nblk > 0 && 16 * (uint32_t)j < nblk + (wop ? B.smis : A.smis);
+    const i32x4 d = uniform(live ? (wop ? B.s : A.s) : none);
+    const uint32_t slot = (uint32_t)(j % kWinSlots);
+    dma_b128(d, lds_win + (slot * 2 + wop) * (kWinBytes / 2) + (wave & 3) * 64 * 16,
+             win_off + (uint32_t)(16 * j));
+  };
 
-  // Prologue: steps 0, 1, 2 in flight.
-  issue(0, S0{});
-  issue(1, S1{});
-  issue(2, S2{});
-  // Each step: wait until only the 2 later steps are outstanding (this step
-  // landed), barrier (visible to all; the slot of the previous step is free),
-  // issue step + 3 into that slot, multiply this step.  The loop runs whole
-  // groups of kStages steps (one exit keeps the 256 accumulators in place);
-  // steps past the end multiply zero tiles.
-  constexpr int kWait = (kStages - 2) * vmem_per_step<PT>();
-  const int64_t nsteps_pad = (nsteps + kStages - 1) / kStages * kStages;
-  for (int64_t s0 = 0; s0 < nsteps_pad; s0 += kStages) {
-    wait_vmcnt<kWait>();
+  // Fragments and scales of one k-step for this wavefront's 128 x 64 tile.
+  struct Frags {
+    i32x8 a[4], b[2];
+    uint32_t sa[4], sb[2];
+  };
+  auto read = [&](int32_t s, Frags& f) {
+    const uint32_t slot = (uint32_t)((s >> 1) & (kSlots - 1));
+    const int ks = (int)(s & 1);
+    const uint8_t* lA = smem + slot * 2 * kStage;
+    const uint8_t* lB = lA + kStage;
+    const int c0 = ks * 4 + half, c1 = c0 + 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = read_frag(lA, wm * 128 + i * 32 + r32, c0, c1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.b[j] = read_frag(lB, bn + j * 32 + r32, c0, c1);
+    if (PT) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.sa[i] = 127u;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.sb[j] = 127u;
+    } else if (SBYTES) {
+      const uint32_t* sc = ssc + (slot * 2 + ks) * 2 * 2 * TM;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.sa[i] = sc[(wm * 128 + i * 32 + r32) * 2 + half];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.sb[j] = sc[2 * TM + (bn + j * 32 + r32) * 2 + half];
+    } else {
+      // block 2s + half of row r: window (smis + 2s + half) / 16 relative to
+      // the tile, byte (smis + 2s + half) % 16; blocks past the range read as
+      // scale code 0 (their codes are zero).
+      const int32_t p = s >> 3;
+      const uint32_t ps0 = (uint32_t)(p % kWinSlots), ps1 = ps0 == kWinSlots - 1 ? 0 : ps0 + 1;
+      const uint32_t u = (uint32_t)(2 * (s & 7) + half);
+      const bool valid = 2 * (uint32_t)s + half < nblk;
+      const uint32_t ta = A.smis + u, tb = B.smis + u;
+      const uint8_t* wA = reinterpret_cast<const uint8_t*>(ssc) + (ta >> 4 ? ps1 : ps0) * kWinBytes +
+                          (ta & 15) + (wm * 128 + r32) * 16;
+      const uint8_t* wB = reinterpret_cast<const uint8_t*>(ssc) + (tb >> 4 ? ps1 : ps0) * kWinBytes +
+                          kWinBytes / 2 + (tb & 15) + (bn + r32) * 16;
+      const uint32_t keep = valid ? 0xFFu : 0u;     // a mask, so the loads stay unconditional
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.sa[i] = (uint32_t)wA[i * 32 * 16] & keep;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f.sb[j] = (uint32_t)wB[j * 32 * 16] & keep;
+    }
+  };
+  // The 8 MFMAs of one k-step; with ISSUE, this wavefront's share of stage
+  // u's loads goes in between them (one load after each MFMA, so the loads
+  // issue while the matrix core is busy).
+  // The asm statements pin the MFMAs inside the compute phase: the operands
+  // are "produced" after the phase's opening barrier and the accumulators
+  // "consumed" before its closing one.
+  auto mma = [&](Frags& f, auto issue_tag, int32_t u) {
+    constexpr bool ISSUE = decltype(issue_tag)::value;
+    asm volatile("" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
+                 "+v"(f.b[1]), "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]),
+                 "+v"(f.sb[0]), "+v"(f.sb[1]));
+    static_for<8>([&](auto k) {
+      constexpr int K = decltype(k)::value, i = K / 2, j = K % 2;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          f.b[j], f.a[i], acc[i][j], 0, 0, 0, (int)f.sb[j], 0, (int)f.sa[i]);
+      if constexpr (ISSUE) stage_dma(u, K);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (ISSUE) issue_stage_scales(u);
+    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                 "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]));
+  };
+  // Barrier that nothing is scheduled across; `fence` also completes this
+  // wavefront's LDS reads first.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    issue(s0 + 3, S3{});
-    compute(s0, S0{});
-    wait_vmcnt<kWait>();
-    __syncthreads();
-    issue(s0 + 4, S0{});
-    compute(s0 + 1, S1{});
-    wait_vmcnt<kWait>();
-    __syncthreads();
-    issue(s0 + 5, S1{});
-    compute(s0 + 2, S2{});
-    wait_vmcnt<kWait>();
-    __syncthreads();
-    issue(s0 + 6, S2{});
-    compute(s0 + 3, S3{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto bare_barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_assert(kSlots == 2, "slot reuse below assumes a 2-slot ring");
+  constexpr int VS = vmem_per_stage<SBYTES>();
+
+  // Ping-pong.  Each k-step s is a memory phase (read step s's fragments
+  // from LDS) and a compute phase (8 MFMAs), separated by workgroup
+  // barriers.  Group 1 runs one phase behind group 0, so on every SIMD one
+  // wavefront multiplies while the other reads LDS.  Phase numbers: group 0
+  // reads step s in phase 2s-1 and multiplies it in phase 2s; group 1 one
+  // phase later.  Stage t (steps 2t, 2t+1) is read in phases 4t-1 .. 4t+2.
+  // Stage t+1 is loaded by group 0 during its compute phase of step 2t
+  // (phase 4t) and by group 1 during that of step 2t-1 (phase 4t-1), into
+  // the slot of stage t-1 (last read in phase 4t-2), interleaved with the
+  // MFMAs; group 0 waits for its share at the end of its compute phase of
+  // step 2t+1, group 1 at the end of its memory phase of step 2t+1 (both
+  // phase 4t+2), so the stage is visible when first read (phase 4t+3).
+  // Stages past the end load zeros into free slots; an odd step count runs
+  // one extra step on zero codes.  Scale window p+2 is loaded at steps 8p+1
+  // (group 1) and 8p+2 (group 0), into the slot of window p-1 (last read at
+  // step 8p-1), and first read at step 8p+8.
+  using On = std::true_type;
+  using Off = std::false_type;
+  if (SWIN) {
+    issue_window(0);
+    issue_window(1);
+  }
+  issue_stage(0);
+  if (grp == 1) {
+    issue_stage(1);                                 // group 0 loads its share at step 0
+    wait_vmcnt<VS>();                               // windows 0, 1 and stage 0 landed
+  } else {
+    wait_vmcnt<0>();
+  }
+  barrier();
+  Frags f;
+  if (grp == 0) {
+    for (int32_t t = 0; t < nstages; ++t) {
+      read(2 * t, f);
+      barrier();
+      mma(f, On{}, t + 1);
+      if (SWIN && (t & 3) == 1) issue_window((t >> 2) + 2);
+      barrier();
+      read(2 * t + 1, f);
+      barrier();
+      mma(f, Off{}, 0);
+      wait_vmcnt<0>();
+      barrier();
+    }
+    bare_barrier();
+  } else {
+    bare_barrier();
+    for (int32_t t = 0; t < nstages; ++t) {
+      read(2 * t, f);
+      barrier();
+      mma(f, Off{}, 0);
+      barrier();
+      read(2 * t + 1, f);
+      wait_vmcnt<0>();
+      barrier();
+      mma(f, On{}, t + 2);
+      if (SWIN && (t & 3) == 0) issue_window((t >> 2) + 2);
+      barrier();
+    }
   }
   // Drain the trailing (zero-range) loads before the LDS goes away.
   wait_vmcnt<0>();
 
   // ---- epilogue: acc[i][j] holds C[m = wm*128 + i*32 + lane%32]
-  //                [n = wn*128 + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
+  //                [n = bn + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
   float mul = 1.0f;
   if (PT) mul = (*g.pta) * (*g.ptb);
 #pragma unroll
@@ -476,10 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     if (ml >= c_rows) continue;
     const int64_t m = m0 + ml;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + j * 32 + q * 8 + half * 4;
+        const int64_t n = n0 + bn + j * 32 + q * 8 + half * 4;
         store4<OUT>(cbase, g.ldc, m, n, g.N, acc[i][j][4 * q] * mul,
                     acc[i][j][4 * q + 1] * mul, acc[i][j][4 * q + 2] * mul,
                     acc[i][j][4 * q + 3] * mul);
@@ -498,17 +636,28 @@ using namespace mxq;
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+template <int KIND, bool PT, bool SW>
+static void launch_kernel(const GemmArgs& g, uint32_t blocks, int out, hipStream_t stream) {
+  if (out == MXQ_OUT_BF16)
+    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_BF16, SW>), dim3(blocks), dim3(kThreads), 0,
+                       stream, g);
+  else
+    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_FP32, SW>), dim3(blocks), dim3(kThreads), 0,
+                       stream, g);
+}
+
+// Scale windows need both operands' scale row strides to be multiples of 16.
 template <int KIND, bool PT>
 static int launch_gemm(GemmArgs& g, int64_t blocks, int out, hipStream_t stream) {
   if (blocks == 0) return MXQ_OK;
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   g.nblocks = (uint32_t)blocks;
-  if (out == MXQ_OUT_BF16)
-    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_BF16>), dim3((uint32_t)blocks), dim3(kThreads),
-                       0, stream, g);
+  if constexpr (PT)
+    launch_kernel<KIND, PT, false>(g, (uint32_t)blocks, out, stream);
+  else if (g.ldsa % 16 == 0 && g.ldsb % 16 == 0)
+    launch_kernel<KIND, PT, true>(g, (uint32_t)blocks, out, stream);
   else
-    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_FP32>), dim3((uint32_t)blocks), dim3(kThreads),
-                       0, stream, g);
+    launch_kernel<KIND, PT, false>(g, (uint32_t)blocks, out, stream);
   return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 

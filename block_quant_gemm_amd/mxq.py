@@ -93,6 +93,14 @@ def _bf16_bits(x):
 # quantization
 # ---------------------------------------------------------------------------
 
+def _scale_buffer(rows, cols, device):
+    """[rows, cols] uint8 view of storage whose row stride is a multiple of 16
+    bytes: the GEMMs read such scales in 16-byte windows (any stride works,
+    byte by byte, more slowly)."""
+    ld = (cols + 15) // 16 * 16
+    return torch.empty((rows, ld), dtype=torch.uint8, device=device)[:, :cols]
+
+
 def mx_quantize_rowwise(x, q=None, scale=None):
     """Row-wise (1x32) MX quantization of a BF16 [M, K] matrix.
 
@@ -102,7 +110,7 @@ def mx_quantize_rowwise(x, q=None, scale=None):
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scale is None:
-        scale = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+        scale = _scale_buffer(M, K // 32, x.device)
     _check(load().mx_quantize_rowwise(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0),
                                       _ptr(scale), scale.stride(0), _stream()))
     return q, scale
@@ -131,7 +139,7 @@ def mx_quantize_colwise(x, offsets=None, M_cap=None, qT=None, scaleT=None,
     if qT is None:
         qT = torch.empty((K, M_cap), dtype=torch.uint8, device=x.device)
     if scaleT is None:
-        scaleT = torch.empty((K, M_cap // 32), dtype=torch.uint8, device=x.device)
+        scaleT = _scale_buffer(K, M_cap // 32, x.device)
     if offsets is not None and offsets_padded is None:
         offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
     _check(load().mx_quantize_colwise(_ptr(x), M, K, x.stride(0), _ptr(offsets), E,

@@ -156,7 +156,9 @@ typedef enum { MXQ_ACC_MFMA_FP8 = 0, MXQ_ACC_FP32 = 1 } mxq_accum;
  *   c            : device output [M, N], row stride ldc elements, BF16 or FP32.
  * Requires K % 32 == 0; lda, ldb % 16 == 0; a, b 16-byte aligned; ldc >= N;
  * (M rows of lda bytes and the scale rows) addressable with 32-bit offsets
- * per 256-row tile.  Scale pointers and strides have no alignment rule.
+ * per 256-row tile.  Scale pointers and strides have no alignment rule;
+ * when ldsa and ldsb are both multiples of 16 the scales are fetched in
+ * 16-byte windows (much less load traffic), otherwise byte by byte.
  * K == 0 writes zeros; M == 0 or N == 0 is a no-op.
  */
 MXQ_API int mx_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, int64_t ldsa,
@@ -215,7 +217,8 @@ MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t ld
  *   For each group e: dW_e[N, K] = Σ_{t in [poff[e], poff[e+1])} at[:, t] · bt[:, t]ᵀ
  *   c : device [E, N, K] with row stride ldc and expert stride N*ldc; an empty
  *       group writes zeros.
- * Requires lda_t, ldb_t % 16 == 0 and 16-byte aligned code pointers.
+ * Requires lda_t, ldb_t % 16 == 0 and 16-byte aligned code pointers.  As for
+ * mx_gemm, scale row strides that are multiples of 16 take the faster path.
  */
 MXQ_API int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t, int64_t ldsa_t,
                           const uint8_t* bt, const uint8_t* bt_scale, int64_t ldb_t, int64_t ldsb_t,

@@ -61,15 +61,37 @@ def test_tiny_linear_forward(out):
     _check(c, Y, S, T, out)
 
 
+def _relayout_scales(s, layout):
+    """Copy of a [rows, nb] scale tensor with another row stride / base offset:
+    'pad16' keeps the quantizer's (stride a multiple of 16: 16-byte windows),
+    'odd' has an odd stride (byte-by-byte path), 'shift5' a stride multiple
+    of 16 with the base 5 bytes past a 16-byte boundary (windows whose first
+    block sits mid-window)."""
+    if layout == "pad16":
+        return s
+    rows, nb = s.shape
+    if layout == "odd":
+        buf = torch.zeros((rows, nb + 1 + (nb % 2)), dtype=torch.uint8, device=s.device)
+        v = buf[:, :nb]
+    else:
+        ld = (nb + 5 + 15) // 16 * 16
+        buf = torch.zeros((rows, ld), dtype=torch.uint8, device=s.device)
+        v = buf[:, 5:5 + nb]
+    v.copy_(s)
+    return v
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (200, 136, 96), (129, 257, 160), (64, 40, 1408),
-                                   (3, 500, 2048)])
+                                   (3, 500, 2048), (300, 264, 1056)])
 @pytest.mark.parametrize("out", OUTS)
-def test_dense_ragged(M, N, K, out):
-    say(f"dense ragged M={M} N={N} K={K} out={out}")
+@pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
+def test_dense_ragged(M, N, K, out, layout):
+    say(f"dense ragged M={M} N={N} K={K} out={out} scales={layout}")
     a = workloads.bf16_normal((M, K), 1.0, seed=M + K, name="ga")
     b = workloads.bf16_normal((N, K), 0.02, seed=N + K, name="gb")
     aq, asc, ah, ash = _quant_rows(a)
     bq, bsc, bh, bsh = _quant_rows(b)
+    asc, bsc = _relayout_scales(asc, layout), _relayout_scales(bsc, layout)
     c = mxq.mx_gemm(aq, asc, bq, bsc, out_dtype=out)
     Y, S = gemm.gemm_ref(mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh))
     _check(c, Y, S, gemm.fp8_mfma_truncation_bound(ah, ash, bh, bsh), out)
@@ -149,12 +171,14 @@ def _grouped_case(counts, N, K, seed):
     ([128, 128, 0, 1, 127, 129], 136, 1408),
 ])
 @pytest.mark.parametrize("out", OUTS)
-def test_grouped_var_m(counts, N, K, out):
-    say(f"grouped var-M counts={counts} N={N} K={K} out={out}")
+@pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
+def test_grouped_var_m(counts, N, K, out, layout):
+    say(f"grouped var-M counts={counts} N={N} K={K} out={out} scales={layout}")
     offs, a, w = _grouped_case(counts, N, K, seed=len(counts) + K)
     E = len(counts)
     aq, asc, ah, ash = _quant_rows(a)
     bq, bsc, bh, bsh = _quant_rows(w)                       # [E*N, K]
+    asc, bsc = _relayout_scales(asc, layout), _relayout_scales(bsc, layout)
     c = mxq.mx_grouped_gemm(aq, asc, bq.view(E, N, K), bsc.view(E, N, K // 32),
                             to_dev(offs), out_dtype=out)
     A, B = mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh)
@@ -209,10 +233,12 @@ def test_grouped_moe_gate_up_sampled():
     ([40, 0, 1, 130, 0, 300, 0], 160, 96),
     ([0, 64], 32, 32),
     ([333, 12, 0, 77], 136, 200),
+    ([700, 33, 1100, 0, 517], 288, 160),
 ])
 @pytest.mark.parametrize("out", OUTS)
-def test_grouped_wgrad(counts, N, K, out):
-    say(f"grouped wgrad counts={counts} N={N} K={K} out={out}")
+@pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
+def test_grouped_wgrad(counts, N, K, out, layout):
+    say(f"grouped wgrad counts={counts} N={N} K={K} out={out} scales={layout}")
     counts = np.array(counts, np.int64)
     offs = workloads.offsets_from_counts(counts)
     E, T = len(counts), int(counts.sum())
@@ -220,6 +246,7 @@ def test_grouped_wgrad(counts, N, K, out):
     x = workloads.bf16_normal((T, K), 1.0, seed=T, name="wx")
     dyT, dysT, poff = mxq.mx_quantize_colwise(to_dev_bf16(dy), to_dev(offs))
     xT, xsT, _ = mxq.mx_quantize_colwise(to_dev_bf16(x), to_dev(offs))
+    dysT, xsT = _relayout_scales(dysT, layout), _relayout_scales(xsT, layout)
     c = mxq.mx_grouped_gemm_wgrad(dyT, dysT, xT, xsT, poff, out_dtype=out)
     ah, ash, bh, bsh, ph = host(dyT), host(dysT), host(xT), host(xsT), host(poff)
     A, B = mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh)
