@@ -38,6 +38,8 @@ constexpr int TS = 128;                           // stage: two k-steps, 128-byt
 constexpr int kThreads = 512;                     // 8 wavefronts, 2 per SIMD
 constexpr int kSlots = 2;                         // LDS ring of stages
 constexpr int kStage = TM * TS;                   // bytes per operand per stage (32 KB)
+constexpr int kCStride = TN * 2 + 16;             // LDS row stride of the staged BF16 tile
+constexpr int kSmem = kSlots * 2 * kStage > TM * kCStride ? kSlots * 2 * kStage : TM * kCStride;
 constexpr int kGroupM = 4;                        // M tiles per rasterization group
 constexpr int kMaxGroups = 256;
 
@@ -309,7 +311,8 @@ template <int KIND, bool PT, int OUT, bool SW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   constexpr bool SBYTES = !PT && !SW;               // per-step scale-byte loads
   constexpr bool SWIN = !PT && SW;                  // scale windows
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSlots * 2 * kStage];  // [slot][A, B]
+  // [slot][A, B] stages; after the k loop, the staged BF16 output tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   // byte path: [slot][k-step][A, B][row][blk] as dwords;
   // windows: [wslot][A, B][row][16 B]
   __shared__ __attribute__((aligned(16)))
@@ -608,6 +611,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   //                [n = bn + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
   float mul = 1.0f;
   if (PT) mul = (*g.pta) * (*g.ptb);
+  const bool staged = OUT == MXQ_OUT_BF16 && n0 + TN <= g.N && (g.ldc & 7) == 0 &&
+                      (reinterpret_cast<uintptr_t>(cbase) & 15) == 0;
+  if (staged) {
+    // Full-width BF16 tile: round into LDS (rows of kCStride bytes; the 16
+    // bytes of padding spread 16 consecutive rows over the banks), then store
+    // whole rows, 16 bytes per lane, two 512-byte rows per instruction.
+    barrier();                                      // every wave's loads drained
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ml = wm * 128 + i * 32 + r32, nl = bn + j * 32 + q * 8 + half * 4;
+          const f32x16& v = acc[i][j];
+          uint2 u;
+          u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q] * mul)) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 1] * mul)) << 16);
+          u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 2] * mul)) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 3] * mul)) << 16);
+          *reinterpret_cast<uint2*>(smem + ml * kCStride + nl * 2) = u;
+        }
+    barrier();
+    const int rsub = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = wave * 32 + it * 2 + rsub;
+      if (row < c_rows) {
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(cbase) + (m0 + row) * g.ldc * 2 +
+                                  n0 * 2 + col * 16) = v;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t ml = wm * 128 + i * 32 + r32;
