@@ -85,17 +85,23 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
 // Column-wise (grouped, zero-padded) MX quantization, transposed output.
 //
 // A workgroup (256 lanes) owns 128 consecutive padded output columns (four
-// 32-blocks along M) by 64 input columns (K).  It loads the 128 source rows
-// (16 B per lane, coalesced along K) into LDS, then each wave quantizes one
-// 32-block: lane pair (2p, 2p+1) holds input columns 2p and 2p+1 for the upper
-// and lower 16 rows of the block, takes a packed-u16 max down its 16 rows and
-// one DPP exchange with its partner, and writes 16 codes for each of its two
-// columns as one 16 B store into the transposed output.
+// 32-blocks along M) and walks kColPasses x 64 input columns (K).  The group
+// table and the source rows of its four blocks are set up once.  Per pass it
+// has the 128 source rows (16 B per lane, whole 128-byte lines along K) in
+// registers, prefetched during the previous pass, writes them to LDS, and
+// each wave quantizes one 32-block: lane pair (2p, 2p+1) holds input columns
+// 2p and 2p+1 for the upper and lower 16 rows of the block, takes a
+// packed-u16 max down its 16 rows and one DPP exchange with its partner, and
+// puts 16 codes for each of its two columns into an LDS staging tile.  The
+// staged 64 x 128 codes then go out as whole 128-byte rows of the transposed
+// output, and the 64 x 4 scales as one dword (or four bytes) per row.
 // ---------------------------------------------------------------------------
 
 constexpr int kColTileM = 128;   // padded output columns per workgroup
-constexpr int kColTileK = 64;    // input columns per workgroup
-constexpr int kColLdsW = 34;     // LDS row stride in dwords (32 + 2 pad)
+constexpr int kColTileK = 64;    // input columns per pass
+constexpr int kColPasses = 4;    // passes per workgroup
+constexpr int kColLdsW = 34;     // LDS row stride of the input tile in dwords (32 + 2 pad)
+constexpr int kColOutW = 144;    // LDS row stride of the staged codes in bytes (128 + 16 pad)
 constexpr int kColMaxGroupsLds = 256;
 
 __global__ __launch_bounds__(256) void k_mx_colwise(
@@ -104,6 +110,8 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     uint8_t* __restrict__ qT, int64_t ldqT, int64_t M_cap,
     uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded) {
   __shared__ uint32_t tile[kColTileM * kColLdsW];
+  __shared__ __attribute__((aligned(16))) uint8_t outq[kColTileK * kColOutW];
+  __shared__ __attribute__((aligned(16))) uint8_t outs[kColTileK * 4];
   __shared__ int64_t s_off[kColMaxGroupsLds + 1];
   __shared__ int64_t s_poff[kColMaxGroupsLds + 1];
   __shared__ int64_t s_src0[4];
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
 
   const int tid = threadIdx.x;
   const int64_t p0 = (int64_t)blockIdx.x * kColTileM;     // first padded column
-  const int64_t k0 = (int64_t)blockIdx.y * kColTileK;     // first input column
+  const int64_t kw0 = (int64_t)blockIdx.y * kColTileK * kColPasses;  // first input column
 
   // Group table: s_off = clamped offsets, s_poff = padded prefix sums.
   const int G = offsets ? E : 1;
@@ -167,59 +175,97 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   }
   __syncthreads();
 
-  // Load 128 rows x 64 columns (8 chunks of 8 BF16 per row).
+  // This lane's loads: tile rows i = 32 u + tid/8 (u = 0..3), 16-byte chunk tid%8.
   const int chunk = tid & 7;
+  const uint16_t* src[4];
+  bool rok[4];
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    int i = pass * 32 + (tid >> 3);                 // tile row 0..127
-    int b = i >> 5, r = i & 31;
-    int64_t kc = k0 + chunk * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < s_nvalid[b] && kc < K)
-      v = *reinterpret_cast<const uint4*>(x + (s_src0[b] + r) * ldx + kc);
-    *reinterpret_cast<uint4*>(&tile[i * kColLdsW + chunk * 4]) = v;
+  for (int u = 0; u < 4; ++u) {
+    const int i = u * 32 + (tid >> 3), b = i >> 5, r = i & 31;
+    rok[u] = r < s_nvalid[b];
+    src[u] = x + (rok[u] ? (s_src0[b] + r) * ldx : 0) + chunk * 8;
   }
-  __syncthreads();
+  auto load = [&](int64_t kb, uint4* v) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (rok[u] && kb + chunk * 8 < K) v[u] = *reinterpret_cast<const uint4*>(src[u] + kb);
+    }
+  };
 
-  // Quantize: wave w -> block w; lane = 2p + h: column pair p, row half h.
   const int w = tid >> 6, lane = tid & 63;
   const int p = lane >> 1, h = lane & 1;
   const int rbase = w * 32 + h * 16;
-  uint32_t vals[16];
+  const bool scale_dword = ((reinterpret_cast<uintptr_t>(scT + (p0 >> 5)) & 3) == 0) &&
+                           (ldsT & 3) == 0 && p0 + kColTileM <= M_cap;
+  uint4 cur[4], nxt[4];
+  load(kw0, cur);
+  for (int pass = 0; pass < kColPasses; ++pass) {
+    const int64_t kb = kw0 + pass * kColTileK;
+    if (kb >= K) break;                             // uniform
 #pragma unroll
-  for (int j = 0; j < 16; ++j) vals[j] = tile[(rbase + j) * kColLdsW + p];
-  u16x2 m = __builtin_bit_cast(u16x2, 0u);
-#pragma unroll
-  for (int j = 0; j < 16; j += 2) m = __builtin_elementwise_max(m, absmax2(vals[j], vals[j + 1]));
-  uint32_t mw = __builtin_bit_cast(uint32_t, m);
-  uint32_t ow = dpp_u32(mw, kQuadXor1);             // partner lane^1: other half
-  u16x2 mm = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ow));
-  uint32_t code0 = mx_scale_code(mm.x);             // column 2p
-  uint32_t code1 = mx_scale_code(mm.y);             // column 2p+1
-  float inv0 = mx_inv_scale(code0 == 0xFFu ? 127u : code0);
-  float inv1 = mx_inv_scale(code1 == 0xFFu ? 127u : code1);
-  uint32_t c0[4], c1[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
-    uint32_t t0 = cvt2_e4m3_sat<false>(bf16_lo(a) * inv0, bf16_lo(b2) * inv0, 0u);
-    c0[j] = cvt2_e4m3_sat<true>(bf16_lo(c) * inv0, bf16_lo(d) * inv0, t0);
-    uint32_t t1 = cvt2_e4m3_sat<false>(bf16_hi(a) * inv1, bf16_hi(b2) * inv1, 0u);
-    c1[j] = cvt2_e4m3_sat<true>(bf16_hi(c) * inv1, bf16_hi(d) * inv1, t1);
-  }
-  if (code0 == 0xFFu) c0[0] = c0[1] = c0[2] = c0[3] = 0x7F7F7F7Fu;
-  if (code1 == 0xFFu) c1[0] = c1[1] = c1[2] = c1[3] = 0x7F7F7F7Fu;
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<uint4*>(&tile[(u * 32 + (tid >> 3)) * kColLdsW + chunk * 4]) = cur[u];
+    if (pass + 1 < kColPasses) load(kb + kColTileK, nxt);
+    __syncthreads();
 
-  const int64_t col = p0 + w * 32;                  // padded column of this block
-  const int64_t k = k0 + 2 * p;
-  if (col < M_cap && k < K) {
-    int64_t o = col + h * 16;
-    *reinterpret_cast<uint4*>(qT + k * ldqT + o) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-    *reinterpret_cast<uint4*>(qT + (k + 1) * ldqT + o) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-    if (h == 0) {
-      scT[k * ldsT + (col >> 5)] = (uint8_t)code0;
-      scT[(k + 1) * ldsT + (col >> 5)] = (uint8_t)code1;
+    // Quantize: wave w -> block w; lane = 2p + h: column pair p, row half h.
+    uint32_t vals[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vals[j] = tile[(rbase + j) * kColLdsW + p];
+    u16x2 m = __builtin_bit_cast(u16x2, 0u);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) m = __builtin_elementwise_max(m, absmax2(vals[j], vals[j + 1]));
+    uint32_t mw = __builtin_bit_cast(uint32_t, m);
+    uint32_t ow = dpp_u32(mw, kQuadXor1);           // partner lane^1: other half
+    u16x2 mm = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ow));
+    uint32_t code0 = mx_scale_code(mm.x);           // column 2p
+    uint32_t code1 = mx_scale_code(mm.y);           // column 2p+1
+    float inv0 = mx_inv_scale(code0 == 0xFFu ? 127u : code0);
+    float inv1 = mx_inv_scale(code1 == 0xFFu ? 127u : code1);
+    uint32_t c0[4], c1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
+      uint32_t t0 = cvt2_e4m3_sat<false>(bf16_lo(a) * inv0, bf16_lo(b2) * inv0, 0u);
+      c0[j] = cvt2_e4m3_sat<true>(bf16_lo(c) * inv0, bf16_lo(d) * inv0, t0);
+      uint32_t t1 = cvt2_e4m3_sat<false>(bf16_hi(a) * inv1, bf16_hi(b2) * inv1, 0u);
+      c1[j] = cvt2_e4m3_sat<true>(bf16_hi(c) * inv1, bf16_hi(d) * inv1, t1);
     }
+    if (code0 == 0xFFu) c0[0] = c0[1] = c0[2] = c0[3] = 0x7F7F7F7Fu;
+    if (code1 == 0xFFu) c1[0] = c1[1] = c1[2] = c1[3] = 0x7F7F7F7Fu;
+    *reinterpret_cast<uint4*>(&outq[(2 * p) * kColOutW + w * 32 + h * 16]) =
+        make_uint4(c0[0], c0[1], c0[2], c0[3]);
+    *reinterpret_cast<uint4*>(&outq[(2 * p + 1) * kColOutW + w * 32 + h * 16]) =
+        make_uint4(c1[0], c1[1], c1[2], c1[3]);
+    if (h == 0) {
+      outs[(2 * p) * 4 + w] = (uint8_t)code0;
+      outs[(2 * p + 1) * 4 + w] = (uint8_t)code1;
+    }
+    __syncthreads();
+
+    // Stores: 64 rows x 128 codes, 8 lanes x 16 B per row; then 64 x 4 scales.
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int row = it * 32 + (tid >> 3), c16 = tid & 7;
+      const int64_t k = kb + row, col = p0 + c16 * 16;
+      if (k < K && col < M_cap)
+        *reinterpret_cast<uint4*>(qT + k * ldqT + col) =
+            *reinterpret_cast<const uint4*>(&outq[row * kColOutW + c16 * 16]);
+    }
+    if (tid < kColTileK && kb + tid < K) {
+      uint8_t* d = scT + (kb + tid) * ldsT + (p0 >> 5);
+      const uint32_t sv = *reinterpret_cast<const uint32_t*>(&outs[tid * 4]);
+      if (scale_dword) {
+        *reinterpret_cast<uint32_t*>(d) = sv;
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+          if (p0 + 32 * bb < M_cap) d[bb] = (uint8_t)(sv >> (8 * bb));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
   }
 }
 
@@ -405,7 +451,7 @@ extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int6
   if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
     return MXQ_ERR_ALIGN;
   dim3 grid((uint32_t)((M_cap + kColTileM - 1) / kColTileM),
-            (uint32_t)((K + kColTileK - 1) / kColTileK));
+            (uint32_t)((K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses)));
   hipLaunchKernelGGL(k_mx_colwise, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E, qT,
                      ldqT, M_cap, scaleT, ldsT, offsets_padded);
   return launch_status();
