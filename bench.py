@@ -39,8 +39,8 @@ HIDDEN, FFN, E, TOKENS, TOP_K = 2048, 1408, 64, 8192, 6
 KFN = {
     "q_row": "k_mx_rowwise",
     "q_col": "k_mx_colwise",
-    "gmm": "k_gemm<1,false,0>",
-    "wgrad": "k_gemm<2,false,0>",
+    "gmm": "k_gemm<1,false,0,true>",
+    "wgrad": "k_gemm<2,false,0,true>",
 }
 
 
