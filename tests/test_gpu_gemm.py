@@ -44,6 +44,10 @@ def _check(c, Y, S, extra, out):
         bare = gemm.check_bf16(host(c), Y, S)
     say(f"  elements {ok.size}: within 1e-5*S+1e-6: {bare.mean():.6f}; "
         f"within that + MFMA allowance: {ok.mean():.6f}")
+    if not ok.all():
+        bad = np.argwhere(~ok)[:12]
+        say(f"  first failures (index, value, oracle): "
+            f"{[(tuple(int(v) for v in i), float(host(c).astype(np.float64)[tuple(i)]) if out == mxq.OUT_FP32 else int(host(c)[tuple(i)]), float(Y[tuple(i)])) for i in bad]}")
     assert ok.all(), f"{(~ok).sum()} elements out of tolerance"
     return bare
 
