@@ -30,6 +30,23 @@ namespace mxq {
 
 constexpr int kRowUnroll = 4;
 
+// Code stores are non-temporal: the big output streams then do not
+// allocate in the caches on their way to HBM (measured 5-15 % faster than
+// plain stores on the expert layer's large operands; non-temporal loads gave
+// no gain).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_stream(void* p, uint4 v) {
+  u32x4 w;
+  w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_stream(void* p, uint2 v) {
+  u32x2 w;
+  w[0] = v.x; w[1] = v.y;
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+}
+
 __device__ __forceinline__ void quant8(uint4 v, uint32_t& lo, uint32_t& hi, uint32_t& code) {
   u16x2 m = __builtin_elementwise_max(absmax2(v.x, v.y), absmax2(v.z, v.w));
   uint32_t am = m.x > m.y ? m.x : m.y;
@@ -74,7 +91,7 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
       uint32_t lo, hi, code;
       quant8(v[u], lo, hi, code);
       if (ok[u]) {
-        *reinterpret_cast<uint2*>(q + (int64_t)row[u] * ldq + col[u]) = make_uint2(lo, hi);
+        store_stream(q + (int64_t)row[u] * ldq + col[u], make_uint2(lo, hi));
         if ((lane & 3u) == 0u) sc[(int64_t)row[u] * lds + (col[u] >> 5)] = (uint8_t)code;
       }
     }
@@ -94,7 +111,10 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
 // packed-u16 max down its 16 rows and one DPP exchange with its partner, and
 // puts 16 codes for each of its two columns into an LDS staging tile.  The
 // staged 64 x 128 codes then go out as whole 128-byte rows of the transposed
-// output, and the 64 x 4 scales as one dword (or four bytes) per row.
+// output, and the 64 x 4 scales as one dword (or four bytes) per row.  The
+// grid is one-dimensional with the K chunks of a column tile consecutive, so
+// the workgroups in flight read whole source rows rather than 512-byte
+// pieces of many rows.
 // ---------------------------------------------------------------------------
 
 constexpr int kColTileM = 128;   // padded output columns per workgroup
@@ -118,8 +138,12 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   __shared__ int32_t s_nvalid[4];
 
   const int tid = threadIdx.x;
-  const int64_t p0 = (int64_t)blockIdx.x * kColTileM;     // first padded column
-  const int64_t kw0 = (int64_t)blockIdx.y * kColTileK * kColPasses;  // first input column
+  // Workgroups along K are consecutive in dispatch order, so the ones in
+  // flight read whole source rows together.
+  const uint32_t nky = (uint32_t)((K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses));
+  const uint32_t bx = blockIdx.x / nky, by = blockIdx.x % nky;
+  const int64_t p0 = (int64_t)bx * kColTileM;             // first padded column
+  const int64_t kw0 = (int64_t)by * kColTileK * kColPasses;  // first input column
 
   // Group table: s_off = clamped offsets, s_poff = padded prefix sums.
   const int G = offsets ? E : 1;
@@ -150,7 +174,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     }
   }
   __syncthreads();
-  if (offsets_padded && blockIdx.x == 0 && blockIdx.y == 0)
+  if (offsets_padded && blockIdx.x == 0)
     for (int g = tid; g <= G; g += blockDim.x) offsets_padded[g] = s_poff[g];
   if (tid < 4) {
     // Source rows of 32-block tid of this tile: find g with
@@ -250,8 +274,8 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
       const int row = it * 32 + (tid >> 3), c16 = tid & 7;
       const int64_t k = kb + row, col = p0 + c16 * 16;
       if (k < K && col < M_cap)
-        *reinterpret_cast<uint4*>(qT + k * ldqT + col) =
-            *reinterpret_cast<const uint4*>(&outq[row * kColOutW + c16 * 16]);
+        store_stream(qT + k * ldqT + col,
+                     *reinterpret_cast<const uint4*>(&outq[row * kColOutW + c16 * 16]));
     }
     if (tid < kColTileK && kb + tid < K) {
       uint8_t* d = scT + (kb + tid) * ldsT + (p0 >> 5);
@@ -450,8 +474,10 @@ extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int6
   (void)need;
   if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
     return MXQ_ERR_ALIGN;
-  dim3 grid((uint32_t)((M_cap + kColTileM - 1) / kColTileM),
-            (uint32_t)((K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses)));
+  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
+  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  dim3 grid((uint32_t)(gx * gy));
   hipLaunchKernelGGL(k_mx_colwise, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E, qT,
                      ldqT, M_cap, scaleT, ldsT, offsets_padded);
   return launch_status();
