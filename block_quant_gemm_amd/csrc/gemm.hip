@@ -40,7 +40,13 @@ constexpr int kSlots = 2;                         // LDS ring of stages
 constexpr int kStage = TM * TS;                   // bytes per operand per stage (32 KB)
 constexpr int kCStride = TN * 2 + 16;             // LDS row stride of the staged BF16 tile
 constexpr int kSmem = kSlots * 2 * kStage > TM * kCStride ? kSlots * 2 * kStage : TM * kCStride;
-constexpr int kGroupM = 4;                        // M tiles per rasterization group
+// M tiles per rasterization group: dense GEMMs walk N with 8 M-tiles (each
+// XCD takes a contiguous run of tiles); grouped variable-M GEMMs with 4,
+// dispatched in plain order so that all XCDs work on neighbouring tiles
+// (measured on the expert-layer shapes: the shared last-level cache then
+// serves the panels every XCD reads).
+constexpr int kGroupMDense = 8;
+constexpr int kGroupMVarM = 4;
 constexpr int kMaxGroups = 256;
 
 // Compile-time loops: f(std::integral_constant<int, I>) for I in [B, E).
@@ -235,15 +241,16 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t m, int64_t 
 
 // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous run of tile indices so tiles sharing operand panels share an L2.
-// Only for kinds whose tiles carry equal work.
+// Used for dense GEMMs.
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t n) {
   const uint32_t X = 8, per = n / X, rem = n % X;
   const uint32_t x = bid % X, i = bid / X;
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
 }
 
-// Tile index -> (tm, tn): groups of kGroupM M-tiles walk N together, so the
-// tiles in flight on one XCD read a few A panels and a few B panels.
+// Tile index -> (tm, tn): groups of G M-tiles walk N together, so the tiles
+// in flight read a few A panels and a few B panels.
+template <int kGroupM>
 __device__ __forceinline__ void raster(uint32_t tile, uint32_t tiles_m, uint32_t tiles_n,
                                        uint32_t& tm, uint32_t& tn) {
   const uint32_t per_group = kGroupM * tiles_n;
@@ -338,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   if (KIND == kDense) {
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
     uint32_t tm, tn;
-    raster(xcd_remap(blockIdx.x, g.nblocks), tiles_m, g.tiles_n, tm, tn);
+    raster<kGroupMDense>(xcd_remap(blockIdx.x, g.nblocks), tiles_m, g.tiles_n, tm, tn);
     m0 = (int64_t)tm * TM;
     n0 = (int64_t)tn * TN;
     c_rows = g.M - m0;
@@ -347,10 +354,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   } else if (KIND == kVarM) {
     group_table(g.offsets, g.E, g.M, s_off, s_start);
     const uint32_t tiles_m = (uint32_t)s_start[g.E];  // data-dependent M-tile count
-    const uint32_t tile = xcd_remap(blockIdx.x, g.nblocks);
+    const uint32_t tile = blockIdx.x;
     if (tile >= tiles_m * g.tiles_n) return;          // surplus workgroup
     uint32_t tm, tn;
-    raster(tile, tiles_m, g.tiles_n, tm, tn);
+    raster<kGroupMVarM>(tile, tiles_m, g.tiles_n, tm, tn);
     int lo = 0, hi = g.E - 1;                         // group e: s_start[e] <= tm < s_start[e+1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
