@@ -124,11 +124,17 @@ constexpr int kColLdsW = 34;     // LDS row stride of the input tile in dwords (
 constexpr int kColOutW = 144;    // LDS row stride of the staged codes in bytes (128 + 16 pad)
 constexpr int kColMaxGroupsLds = 256;
 
+// ROW (dual-axis quantization): the same pass also emits the row-wise (1x32)
+// codes and scales of every source row it holds.  Lane tid has 8 consecutive
+// columns of a row, and the 4 lanes of a DPP quad one 32-block of it (K is a
+// multiple of 32), so the row quantizer's block step applies unchanged.
+template <bool ROW>
 __global__ __launch_bounds__(256) void k_mx_colwise(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const int64_t* __restrict__ offsets, int32_t E,
     uint8_t* __restrict__ qT, int64_t ldqT, int64_t M_cap,
-    uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded) {
+    uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ sc, int64_t lds) {
   __shared__ uint32_t tile[kColTileM * kColLdsW];
   __shared__ __attribute__((aligned(16))) uint8_t outq[kColTileK * kColOutW];
   __shared__ __attribute__((aligned(16))) uint8_t outs[kColTileK * 4];
@@ -202,12 +208,14 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   // This lane's loads: tile rows i = 32 u + tid/8 (u = 0..3), 16-byte chunk tid%8.
   const int chunk = tid & 7;
   const uint16_t* src[4];
+  int64_t srow[4];
   bool rok[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = u * 32 + (tid >> 3), b = i >> 5, r = i & 31;
     rok[u] = r < s_nvalid[b];
-    src[u] = x + (rok[u] ? (s_src0[b] + r) * ldx : 0) + chunk * 8;
+    srow[u] = rok[u] ? s_src0[b] + r : 0;
+    src[u] = x + srow[u] * ldx + chunk * 8;
   }
   auto load = [&](int64_t kb, uint4* v) {
 #pragma unroll
@@ -231,6 +239,20 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     for (int u = 0; u < 4; ++u)
       *reinterpret_cast<uint4*>(&tile[(u * 32 + (tid >> 3)) * kColLdsW + chunk * 4]) = cur[u];
     if (pass + 1 < kColPasses) load(kb + kColTileK, nxt);
+    if (ROW) {
+      // Row-wise codes of the rows held in registers (every lane takes part
+      // in the quad exchanges; only valid rows and columns are stored).
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t lo, hi, code;
+        quant8(cur[u], lo, hi, code);
+        const int64_t k = kb + chunk * 8;
+        if (rok[u] && k < K) {
+          store_stream(q + srow[u] * ldq + k, make_uint2(lo, hi));
+          if ((chunk & 3) == 0) sc[srow[u] * lds + (k >> 5)] = (uint8_t)code;
+        }
+      }
+    }
     __syncthreads();
 
     // Quantize: wave w -> block w; lane = 2p + h: column pair p, row half h.
@@ -478,8 +500,33 @@ extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int6
   const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
   if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   dim3 grid((uint32_t)(gx * gy));
-  hipLaunchKernelGGL(k_mx_colwise, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E, qT,
-                     ldqT, M_cap, scaleT, ldsT, offsets_padded);
+  hipLaunchKernelGGL(k_mx_colwise<false>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
+                     qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, nullptr, 0, nullptr, 0);
+  return launch_status();
+}
+
+extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const int64_t* offsets, int32_t E, uint8_t* q, int64_t ldq,
+                                uint8_t* scale, int64_t lds, uint8_t* qT, int64_t ldqT,
+                                int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
+                                int64_t* offsets_padded, hipStream_t stream) {
+  if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (offsets && (E < 1 || E > kColMaxGroupsLds)) return MXQ_ERR_SHAPE;
+  if (K == 0 || M_cap == 0) return MXQ_OK;
+  if (!qT || !scaleT || (M > 0 && (!x || !q || !scale))) return MXQ_ERR_NULL;
+  if (K % 32 != 0 || M_cap % 32 != 0 || ldqT < M_cap || ldsT < M_cap / 32 || ldx < K ||
+      ldq < K || lds < K / 32)
+    return MXQ_ERR_SHAPE;
+  if (!offsets && M_cap < (M + 31) / 32 * 32) return MXQ_ERR_SHAPE;
+  if (ldqT % 16 != 0 || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(qT, 16) ||
+      (x && !aligned(x, 16)) || (q && !aligned(q, 16)))
+    return MXQ_ERR_ALIGN;
+  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
+  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  dim3 grid((uint32_t)(gx * gy));
+  hipLaunchKernelGGL(k_mx_colwise<true>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
+                     qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, q, ldq, scale, lds);
   return launch_status();
 }
 

@@ -27,6 +27,8 @@ _SIGS = {
     "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _i64,
                                            _p, _i64, _p, _p]),
+    "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _i64,
+                                        _p, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_quantize_per_tensor": (ctypes.c_int, [_p, _i64, _p, _p, _p, _sz, _p]),
     "mx_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64,
                                _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
@@ -146,6 +148,35 @@ def mx_quantize_colwise(x, offsets=None, M_cap=None, qT=None, scaleT=None,
                                       _ptr(qT), qT.stride(0), M_cap, _ptr(scaleT),
                                       scaleT.stride(0), _ptr(offsets_padded), _stream()))
     return qT, scaleT, offsets_padded
+
+
+def mx_quantize_dual(x, offsets=None, M_cap=None, q=None, scale=None, qT=None, scaleT=None,
+                     offsets_padded=None):
+    """Row-wise and (grouped) column-wise MX quantization from one read of x.
+
+    Returns (codes [M, K], scales [M, K/32], codesT [K, M_cap],
+    scalesT [K, M_cap/32], offsets_padded or None), each equal to what
+    mx_quantize_rowwise / mx_quantize_colwise return."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = 0 if offsets is None else offsets.numel() - 1
+    if M_cap is None:
+        M_cap = colwise_capacity(M, E or None)
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = _scale_buffer(M, K // 32, x.device)
+    if qT is None:
+        qT = torch.empty((K, M_cap), dtype=torch.uint8, device=x.device)
+    if scaleT is None:
+        scaleT = _scale_buffer(K, M_cap // 32, x.device)
+    if offsets is not None and offsets_padded is None:
+        offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
+    _check(load().mx_quantize_dual(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q),
+                                   q.stride(0), _ptr(scale), scale.stride(0), _ptr(qT),
+                                   qT.stride(0), M_cap, _ptr(scaleT), scaleT.stride(0),
+                                   _ptr(offsets_padded), _stream()))
+    return q, scale, qT, scaleT, offsets_padded
 
 
 def workspace_size(op, n, a1=0, a2=0, a3=0):

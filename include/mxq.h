@@ -118,6 +118,28 @@ MXQ_API int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t
                         int64_t* offsets_padded, hipStream_t stream);
 
 /*
+ * Dual-axis MX quantization: the row-wise copy of mx_quantize_rowwise and the
+ * (grouped) column-wise copy of mx_quantize_colwise from one read of x
+ * ([HP329] §3.1: an MX weight keeps row data + scale and col data + scale;
+ * §8.1: both are produced once from the master copy after the optimizer step,
+ * while activations and gradients are quantized on the fly and feed both the
+ * dgrad and the wgrad products).  Every output is bit-identical to the
+ * corresponding single-axis call.
+ *   x, M, K, ldx, offsets, E                 : as for mx_quantize_colwise.
+ *   q, ldq, scale, lds                        : as for mx_quantize_rowwise.
+ *   qT, ldqT, M_cap, scaleT, ldsT, offsets_padded : as for mx_quantize_colwise.
+ * Requires the conditions of both calls (K % 32 == 0, ldq % 16 == 0, q
+ * 16-byte aligned, and those of mx_quantize_colwise).  M == 0 writes only the
+ * zero padding of the column copy; K == 0 or M_cap == 0 is a no-op.
+ */
+MXQ_API int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     const int64_t* offsets, int32_t E,
+                     uint8_t* q, int64_t ldq, uint8_t* scale, int64_t lds,
+                     uint8_t* qT, int64_t ldqT, int64_t M_cap,
+                     uint8_t* scaleT, int64_t ldsT,
+                     int64_t* offsets_padded, hipStream_t stream);
+
+/*
  * Per-tensor current-scaling FP8 E4M3 ([HP329] §3.2 current scaling,
  * "scale = valid(amax) ? amax / format_max : 1.0", FP32 scale; [FPBLOG] §七.2
  * first pass finds amax, second pass quantizes).

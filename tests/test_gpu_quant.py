@@ -158,6 +158,112 @@ def test_colwise_matches_rowwise_of_transpose_on_gpu():
 
 
 # ---------------------------------------------------------------------------
+# dual-axis (row and column copies from one read)
+# ---------------------------------------------------------------------------
+
+def _check_dual(x, out, offs=None):
+    """Compare mx_quantize_dual's five outputs with the oracle's row-wise and
+    (grouped) column-wise quantization of the same BF16 matrix."""
+    q, s, qT, sT, poff = out
+    M, K = x.shape
+    rc, rs = mx.mx_quantize_rowwise(x)
+    assert np.array_equal(host(s), rs), "row scales"
+    assert np.array_equal(host(q), rc), "row codes"
+    if offs is None:
+        # one group of all rows: padded with zero rows to a multiple of 32
+        cc, cs, rpoff = mx.mx_quantize_grouped_colwise(x, np.array([0, M], np.int64))
+    else:
+        cc, cs, rpoff = mx.mx_quantize_grouped_colwise(x, offs)
+        assert np.array_equal(host(poff), rpoff)
+    Mp = int(rpoff[-1])
+    qh, sh = host(qT), host(sT)
+    assert np.array_equal(qh[:, :cc.shape[1]], cc) and np.array_equal(sh[:, :cs.shape[1]], cs)
+    assert np.all(qh[:, Mp:] == 0) and np.all(sh[:, Mp // 32:] == 0), "padding"
+
+
+@pytest.mark.parametrize("M,K", [(32, 32), (256, 96), (160, 1408), (97, 2080), (1, 64)])
+def test_dual_plain(M, K):
+    say(f"dual M={M} K={K}")
+    x = workloads.bf16_normal((M, K), 1.0, seed=K + M, name="dp", outlier_frac=0.01,
+                              outlier_scale=100.0)
+    _check_dual(x, mxq.mx_quantize_dual(to_dev_bf16(x)))
+
+
+@pytest.mark.parametrize("counts", [
+    [40, 0, 1, 32, 0, 70, 0],
+    [0, 0, 0, 5],
+    [300],
+    [1] * 9 + [0] * 3 + [77],
+])
+def test_dual_grouped(counts):
+    say(f"dual grouped counts={counts}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    M, K = int(counts.sum()), 224
+    x = workloads.bf16_normal((M, K), 1e-3, seed=int(M) + 1, name="dg", outlier_frac=0.01,
+                              outlier_scale=30.0)
+    _check_dual(x, mxq.mx_quantize_dual(to_dev_bf16(x), to_dev(offs)), offs)
+
+
+def test_dual_special_blocks():
+    """NaN, Inf, zero and subnormal blocks along both axes."""
+    x = workloads.bf16_normal((64, 96), 1.0, seed=5, name="ds")
+    x[3, 40] = 0x7F80           # +Inf: row block 1 of row 3, column block 0 of column 40
+    x[40, 7] = 0x7FC1           # NaN
+    x[32:64, 64:96] = 0         # an all-zero 32 x 32 corner
+    x[0:32, 64] = 0x0001        # BF16 subnormals down one column
+    _check_dual(x, mxq.mx_quantize_dual(to_dev_bf16(x)))
+
+
+def test_dual_strided_untouched():
+    M, K = 70, 160
+    ldx = K + 40
+    big = workloads.bf16_normal((M, ldx), 1.0, seed=11, name="dsu", outlier_frac=0.02,
+                                outlier_scale=50.0)
+    xd = to_dev_bf16(big)[:, :K]
+    qbuf = torch.full((M, K + 32), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((M, K // 32 + 3), 0xCD, dtype=torch.uint8, device="cuda")
+    out = mxq.mx_quantize_dual(xd, q=qbuf[:, :K], scale=sbuf[:, :K // 32])
+    x = np.ascontiguousarray(big[:, :K])
+    _check_dual(x, out)
+    assert np.all(host(qbuf)[:, K:] == 0xAB) and np.all(host(sbuf)[:, K // 32:] == 0xCD)
+
+
+def test_dual_empty_rows_pads_only():
+    offs = np.array([0, 0, 0], np.int64)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, s, qT, sT, poff = mxq.mx_quantize_dual(x, to_dev(offs))
+    assert q.shape == (0, 64) and np.array_equal(host(poff), offs)
+    assert int(host(qT).max(initial=0)) == 0 and int(host(sT).max(initial=0)) == 0
+
+
+def test_dual_matches_single_axis_calls_full_size():
+    """dGU [49152, 2816] with the Zipf expert counts: every byte of the dual
+    outputs equals the row-wise and grouped column-wise kernels' outputs, and
+    the oracle checks 64 sampled rows and 32 sampled columns."""
+    say("dual dGU 49152x2816 vs single-axis kernels and sampled oracle")
+    counts = workloads.moe_counts(0)
+    offs = workloads.offsets_from_counts(counts)
+    dGU = workloads.moe_backward(0)["dGU"]
+    xd, od = to_dev_bf16(dGU), to_dev(offs)
+    q, s, qT, sT, poff = mxq.mx_quantize_dual(xd, od)
+    q1, s1 = mxq.mx_quantize_rowwise(xd)
+    qT1, sT1, poff1 = mxq.mx_quantize_colwise(xd, od)
+    assert torch.equal(q, q1) and torch.equal(s, s1)
+    assert torch.equal(qT, qT1) and torch.equal(sT, sT1) and torch.equal(poff, poff1)
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(dGU.shape[0], 64, replace=False))
+    rc, rs = mx.mx_quantize_rowwise(np.ascontiguousarray(dGU[rows]))
+    ri = torch.from_numpy(rows).cuda()
+    assert np.array_equal(host(q[ri]), rc) and np.array_equal(host(s[ri]), rs)
+    cols = rng.choice(dGU.shape[1], 32, replace=False)
+    cc, cs, rpoff = mx.mx_quantize_grouped_colwise(np.ascontiguousarray(dGU[:, cols]), offs)
+    ci = torch.from_numpy(cols).cuda()
+    Mp = int(rpoff[-1])
+    assert np.array_equal(host(qT[ci])[:, :Mp], cc) and np.array_equal(host(sT[ci])[:, :Mp // 32], cs)
+
+
+# ---------------------------------------------------------------------------
 # per-tensor
 # ---------------------------------------------------------------------------
 
