@@ -9,7 +9,8 @@ Step (all on one HIP stream, inputs resident in HBM):
   wgrad     dW_dn[e] = dY_eᵀ·h_e and dW_gu[e] = dGU_eᵀ·X_e over each expert's
             tokens (grouped column quantization, groups padded to 32)
   quantization of X, h, dY, dGU (row and grouped-column copies) and of W_gu,
-  W_dn (row and column copies) every step.
+  W_dn (row and column copies) every step, each tensor in one dual-axis pass
+  (--separate-quant: one row-wise and one column-wise pass per tensor).
 Synthetic inputs: 8192 tokens x top-6 = 49152 rows, expert counts drawn as a
 multinomial over Zipf(1.1) expert probabilities (seed 0); BF16 N(0,1)
 activations, N(0,0.02) weights, N(0,1e-3) gradients; h and dGU stand in for
@@ -33,12 +34,14 @@ METRIC = "MXFP8 grouped-GEMM TFLOP/s incl. quant (fwd+dgrad+wgrad); % MX-FP8 pea
 PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense MX-FP8 (E4M3) matrix peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 MX_BYTES_PER_ELT = 2 + 1 + 1 / 32   # BF16 in, E4M3 code + E8M0 per 32 out
+DUAL_BYTES_PER_ELT = 2 + 2 * (1 + 1 / 32)   # BF16 in once, row and column copies out
 HIDDEN, FFN, E, TOKENS, TOP_K = 2048, 1408, 64, 8192, 6
 
 # kernel-function names as rocprofv3 reports them
 KFN = {
     "q_row": "k_mx_rowwise",
-    "q_col": "k_mx_colwise",
+    "q_col": "k_mx_colwise<false>",
+    "q_dual": "k_mx_colwise<true>",
     "gmm": "k_gemm<1,false,0,true>",
     "wgrad": "k_gemm<2,false,0,true>",
 }
@@ -54,6 +57,8 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="quantize each tensor with separate row-wise and column-wise passes")
     return ap.parse_args()
 
 
@@ -118,7 +123,29 @@ def main():
 
     T = Timer(torch)
 
-    def step():
+    def step_dual():
+        # forward (each tensor's row and column copies come from one pass)
+        xq, xs, xT, xTs, poff = T.run("q_dual", mxq.mx_quantize_dual, X, offs_d)
+        wq, ws, guT, guTs, _ = T.run("q_dual", mxq.mx_quantize_dual, Wgu, w_off_gu)
+        gu = T.run("gmm", mxq.mx_grouped_gemm, xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                   ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
+        hq, hs, hT, hTs, _ = T.run("q_dual", mxq.mx_quantize_dual, h, offs_d)
+        dq, dsc, dnT, dnTs, _ = T.run("q_dual", mxq.mx_quantize_dual, Wdn, w_off_dn)
+        y = T.run("gmm", mxq.mx_grouped_gemm, hq, hs, dq.view(E, HIDDEN, FFN),
+                  dsc.view(E, HIDDEN, FFN // 32), offs_d)
+        # dgrad
+        gq, gs, dyT, dyTs, _ = T.run("q_dual", mxq.mx_quantize_dual, dY, offs_d)
+        bq, bs = mxq.expert_view(dnT, dnTs, E, HIDDEN)          # [E, 1408, 2048]
+        dh = T.run("gmm", mxq.mx_grouped_gemm, gq, gs, bq, bs, offs_d)
+        uq, us, duT, duTs, _ = T.run("q_dual", mxq.mx_quantize_dual, dGU, offs_d)
+        bq2, bs2 = mxq.expert_view(guT, guTs, E, 2 * FFN)       # [E, 2048, 2816]
+        dx = T.run("gmm", mxq.mx_grouped_gemm, uq, us, bq2, bs2, offs_d)
+        # wgrad
+        dwdn = T.run("wgrad", mxq.mx_grouped_gemm_wgrad, dyT, dyTs, hT, hTs, poff)
+        dwgu = T.run("wgrad", mxq.mx_grouped_gemm_wgrad, duT, duTs, xT, xTs, poff)
+        return gu, y, dh, dx, dwdn, dwgu
+
+    def step_separate():
         # forward
         xq, xs = T.run("q_row", mxq.mx_quantize_rowwise, X)
         wq, ws = T.run("q_row", mxq.mx_quantize_rowwise, Wgu)
@@ -146,6 +173,7 @@ def main():
         dwgu = T.run("wgrad", mxq.mx_grouped_gemm_wgrad, duT, duTs, xT, xTs, poff)
         return gu, y, dh, dx, dwdn, dwgu
 
+    step = step_separate if args.separate_quant else step_dual
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -168,7 +196,12 @@ def main():
                   M * 2 * FFN],
         "q_col": [E * HIDDEN * FFN, E * 2 * FFN * HIDDEN, M * HIDDEN, M * FFN, M * 2 * FFN,
                   M * HIDDEN],
+        "q_dual": [M * HIDDEN, E * 2 * FFN * HIDDEN, M * FFN, E * HIDDEN * FFN, M * HIDDEN,
+                   M * 2 * FFN],
     }
+    quant_bpe = {"q_row": MX_BYTES_PER_ELT, "q_col": MX_BYTES_PER_ELT,
+                 "q_dual": DUAL_BYTES_PER_ELT}
+    qkeys = [k for k in ("q_row", "q_col", "q_dual") if k in avg_ms_keys(T)]
     gemm_flops = {
         "gmm": [2 * M * 2 * FFN * HIDDEN, 2 * M * HIDDEN * FFN, 2 * M * FFN * HIDDEN,
                 2 * M * HIDDEN * 2 * FFN],
@@ -178,8 +211,8 @@ def main():
     n_launch = T.count()
     per_step_ms = {k: avg_ms[k] * n_launch[k] / args.steps for k in avg_ms}
     breakdown = {}
-    for k in ("q_row", "q_col"):
-        work = sum(quant_elts[k]) * MX_BYTES_PER_ELT
+    for k in qkeys:
+        work = sum(quant_elts[k]) * quant_bpe[k]
         breakdown[KFN[k]] = {
             "launches_per_step": n_launch[k] // args.steps, "ms_per_step": per_step_ms[k],
             "avg_launch_us": avg_ms[k] * 1e3,
@@ -193,8 +226,8 @@ def main():
             "TFLOP_per_s": work / (per_step_ms[k] * 1e-3) / 1e12,
             "frac_mfma_peak": work / (per_step_ms[k] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS}
     gemm_ms = per_step_ms["gmm"] + per_step_ms["wgrad"]
-    quant_ms = per_step_ms["q_row"] + per_step_ms["q_col"]
-    quant_bytes = (sum(quant_elts["q_row"]) + sum(quant_elts["q_col"])) * MX_BYTES_PER_ELT
+    quant_ms = sum(per_step_ms[k] for k in qkeys)
+    quant_bytes = sum(sum(quant_elts[k]) * quant_bpe[k] for k in qkeys)
 
     dom = max(per_step_ms, key=per_step_ms.get)
     if dom in gemm_flops:
@@ -203,7 +236,7 @@ def main():
         roof = {"kernel": KFN[dom], "bound": "mfma", "achieved": achieved,
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS}
     else:
-        per_launch = sum(quant_elts[dom]) * MX_BYTES_PER_ELT / len(quant_elts[dom])
+        per_launch = sum(quant_elts[dom]) * quant_bpe[dom] / len(quant_elts[dom])
         achieved = per_launch / (avg_ms[dom] * 1e-3) / 1e9
         roof = {"kernel": KFN[dom], "bound": "hbm", "achieved": achieved,
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS}
@@ -229,13 +262,20 @@ def main():
                    "top_k": TOP_K, "rows": M, "experts": E, "hidden": HIDDEN,
                    "moe_ffn": FFN, "expert_counts": "multinomial over Zipf(1.1), seed %d" % args.seed,
                    "max_expert_rows": int(counts.max()), "min_expert_rows": int(counts.min()),
-                   "weights_quantized_each_step": True, "algorithmic_flops": flops},
+                   "weights_quantized_each_step": True,
+                   "quantization": "separate row and column passes" if args.separate_quant
+                   else "dual-axis (one pass per tensor)",
+                   "algorithmic_flops": flops},
         "pct_mx_fp8_peak": 100.0 * value / PEAK_MFMA_TFLOPS,
         "roofline": roof,
         "cpu_baseline": cpu,
         "components": components,
     }
     print(json.dumps(line), flush=True)
+
+
+def avg_ms_keys(T):
+    return set(T.ev)
 
 
 def measured_traffic(kernel):
