@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
 // 32-blocks along M) and walks kColPasses x 64 input columns (K).  The group
 // table and the source rows of its four blocks are set up once.  Per pass it
 // has the 128 source rows (16 B per lane, whole 128-byte lines along K) in
-// registers, prefetched during the previous pass, writes them to LDS, and
+// registers, prefetched two passes ahead, writes them to LDS, and
 // each wave quantizes one 32-block: lane pair (2p, 2p+1) holds input columns
 // 2p and 2p+1 for the upper and lower 16 rows of the block, takes a
 // packed-u16 max down its 16 rows and one DPP exchange with its partner, and
@@ -123,6 +123,7 @@ constexpr int kColPasses = 4;    // passes per workgroup
 constexpr int kColLdsW = 34;     // LDS row stride of the input tile in dwords (32 + 2 pad)
 constexpr int kColOutW = 144;    // LDS row stride of the staged codes in bytes (128 + 16 pad)
 constexpr int kColMaxGroupsLds = 256;
+constexpr int kColDualGroup = 4;  // column tiles per dispatch block (dual-axis)
 
 // ROW (dual-axis quantization): the same pass also emits the row-wise (1x32)
 // codes and scales of every source row it holds.  Lane tid has 8 consecutive
@@ -145,9 +146,21 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
 
   const int tid = threadIdx.x;
   // Workgroups along K are consecutive in dispatch order, so the ones in
-  // flight read whole source rows together.
+  // flight read whole source rows together.  With ROW, blocks of kColDualGroup
+  // column tiles take the K chunks together (4 adjacent tiles per K chunk), so
+  // the transposed stores in flight also form 512-byte runs of each output row.
   const uint32_t nky = (uint32_t)((K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses));
-  const uint32_t bx = blockIdx.x / nky, by = blockIdx.x % nky;
+  uint32_t bx, by;
+  if (ROW) {
+    const uint32_t ngx = gridDim.x / nky, G = kColDualGroup;
+    const uint32_t per = G * nky, grp = blockIdx.x / per, in = blockIdx.x % per;
+    const uint32_t gw = ngx - grp * G < G ? ngx - grp * G : G;
+    bx = grp * G + in % gw;
+    by = in / gw;
+  } else {
+    bx = blockIdx.x / nky;
+    by = blockIdx.x % nky;
+  }
   const int64_t p0 = (int64_t)bx * kColTileM;             // first padded column
   const int64_t kw0 = (int64_t)by * kColTileK * kColPasses;  // first input column
 
@@ -230,15 +243,16 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   const int rbase = w * 32 + h * 16;
   const bool scale_dword = ((reinterpret_cast<uintptr_t>(scT + (p0 >> 5)) & 3) == 0) &&
                            (ldsT & 3) == 0 && p0 + kColTileM <= M_cap;
-  uint4 cur[4], nxt[4];
+  uint4 cur[4], nxt[4], nx2[4];                     // passes p, p+1 and p+2 in flight
   load(kw0, cur);
+  if (kColPasses > 1) load(kw0 + kColTileK, nxt);
   for (int pass = 0; pass < kColPasses; ++pass) {
     const int64_t kb = kw0 + pass * kColTileK;
     if (kb >= K) break;                             // uniform
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       *reinterpret_cast<uint4*>(&tile[(u * 32 + (tid >> 3)) * kColLdsW + chunk * 4]) = cur[u];
-    if (pass + 1 < kColPasses) load(kb + kColTileK, nxt);
+    if (pass + 2 < kColPasses) load(kb + 2 * kColTileK, nx2);
     if (ROW) {
       // Row-wise codes of the rows held in registers (every lane takes part
       // in the quad exchanges; only valid rows and columns are stored).
@@ -311,7 +325,10 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < 4; ++u) {
+      cur[u] = nxt[u];
+      nxt[u] = nx2[u];
+    }
   }
 }
 
