@@ -7,14 +7,17 @@
 // groups); "Transformer 与 LLM（06）：浮点格式、数值稳定性与混合精度" §五
 // (FP32 accumulation, one rounding to BF16 at the end).
 //
-// Tiling.  A workgroup of 256 lanes (4 wavefronts, 2 x 2) computes a 256 x 256
-// output tile; each wavefront owns 128 x 128 = 4 x 4 MFMA tiles of 32 x 32
-// (256 FP32 accumulators per lane).  The K loop steps 64 codes (two
-// 32-blocks, one MFMA deep) at a time.  Operand tiles go from HBM straight
-// into LDS with buffer_load_dwordx4 ... lds (no register staging) through a
-// 4-slot ring, so three steps are in flight while one is multiplied; one
-// barrier per step.  Rows and K positions outside the operand read as zero
-// through the buffer descriptor's range check.
+// Tiling.  A workgroup of 512 lanes (8 wavefronts, two per SIMD) computes a
+// 256 x 256 output tile; each wavefront owns 128 x 64 = 4 x 2 MFMA tiles of
+// 32 x 32 (128 FP32 accumulators per lane).  The K loop steps 64 codes (two
+// 32-blocks, one MFMA deep) at a time; operand tiles go from HBM straight
+// into LDS with buffer_load_dwordx4 ... lds (no register staging) in stages
+// of two k-steps (128-byte row pieces) through a 2-slot ring.  The two
+// wavefronts of a SIMD ping-pong: one multiplies while the other reads its
+// next fragments from LDS.  Rows and K positions outside the operand read as
+// zero through the buffer descriptor's range check.  Dense and variable-M
+// grids have one workgroup per CU walking tiles; variable K has one
+// workgroup per tile.
 //
 // Matrix instruction.  v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane l,
 // 32 codes of row l%32: bytes 0-15 are k = 16h .. 16h+15 and bytes 16-31 are
