@@ -387,8 +387,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   } else {
     // variable K: tile = (e, tm over rows of A = dW rows, tn over rows of B =
     // dW cols).  Work per tile is proportional to the group's tokens, so the
-    // plain dispatch order (round-robin over XCDs) is kept for balance.
-    const uint32_t tile = tile_i;
+    // dispatch stays in tile order for balance, except that within each block
+    // of 64 workgroups (8 per XCD, dispatched round-robin) workgroup
+    // 64q + 8r + x takes tile 64q + 8x + r: 8 consecutive tiles, which share
+    // an A panel, then run on one XCD and share its L2.
+    uint32_t tile = tile_i;
+    if ((tile | 63u) < ntiles) tile = (tile & ~63u) | ((tile & 7u) << 3) | ((tile >> 3) & 7u);
     const uint32_t tn = tile % g.tiles_n, tmg = tile / g.tiles_n;
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
     const int e = (int)(tmg / tiles_m);
