@@ -15,9 +15,7 @@
 // of two k-steps (128-byte row pieces) through a 2-slot ring.  The two
 // wavefronts of a SIMD ping-pong: one multiplies while the other reads its
 // next fragments from LDS.  Rows and K positions outside the operand read as
-// zero through the buffer descriptor's range check.  Dense and variable-M
-// grids have one workgroup per CU walking tiles; variable K has one
-// workgroup per tile.
+// zero through the buffer descriptor's range check.
 //
 // Matrix instruction.  v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane l,
 // 32 codes of row l%32: bytes 0-15 are k = 16h .. 16h+15 and bytes 16-31 are
@@ -123,7 +121,7 @@ struct GemmArgs {
   int64_t M, N, K;
   void* c; int64_t ldc;
   uint32_t tiles_n;                                 // output tiles along N
-  uint32_t ntiles;                                  // output tiles (dense, variable K)
+  uint32_t nblocks;                                 // grid size (for the XCD remap)
 };
 
 // One operand of a workgroup: codes and scales as buffer resources whose
@@ -183,9 +181,9 @@ struct LaneOffsets {
   uint32_t sblk;            // blk (0 or 1) of the lane's scale entry
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(const OpTile& t, int tid) {
+__device__ __forceinline__ LaneOffsets lane_offsets(const OpTile& t) {
   LaneOffsets o;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int rsub = lane >> 3, slot = lane & 7;
   o.kc0 = (uint32_t)((slot ^ (rsub >> 1)) * 16);
 #pragma unroll
@@ -330,46 +328,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   __shared__ int64_t s_off[KIND == kVarM ? kMaxGroups + 1 : 1];
   __shared__ int32_t s_start[KIND == kVarM ? kMaxGroups + 1 : 1];
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar branches
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
   // Wavefronts w and w + 4 share a SIMD.  Group grp = w / 4 owns output
   // columns [128 grp, 128 grp + 128) of the tile; within it wavefront w
   // computes rows [128 wm, +128) x columns [bn, bn + 64).
   const int grp = wave >> 2, qw = wave & 3;
   const int wm = qw >> 1;
   const int bn = grp * 128 + (qw & 1) * 64;
-
-  // Workgroups walk tiles blockIdx.x, + gridDim.x, ...: a grid of one
-  // workgroup per CU keeps every CU busy and issues one tile's output stores
-  // right before the next tile's first loads.
-  uint32_t ntiles = g.ntiles;
-  if (KIND == kVarM) {
-    group_table(g.offsets, g.E, g.M, s_off, s_start);
-    ntiles = (uint32_t)s_start[g.E] * g.tiles_n;     // data-dependent tile count
-  }
-  for (uint32_t tile_i = blockIdx.x; tile_i < ntiles; tile_i += gridDim.x) {
-  // The lane index is re-read per tile (an opaque copy), so that nothing
-  // derived from it is hoisted out of the tile loop and held in registers
-  // across the k loop.
-  int t;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
-  const int lane = t & 63;
   const int r32 = lane & 31, half = lane >> 5;
-  // ---- map the tile to (group, m0, n0) ----
+
+  // ---- map the workgroup to (group, m0, n0) ----
   int64_t m0 = 0, n0 = 0, kdim = g.K, c_rows = 0;
   void* cbase = g.c;
   OpTile A, B;
   if (KIND == kDense) {
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
     uint32_t tm, tn;
-    raster<kGroupMDense>(xcd_remap(tile_i, ntiles), tiles_m, g.tiles_n, tm, tn);
+    raster<kGroupMDense>(xcd_remap(blockIdx.x, g.nblocks), tiles_m, g.tiles_n, tm, tn);
     m0 = (int64_t)tm * TM;
     n0 = (int64_t)tn * TN;
     c_rows = g.M - m0;
     A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
     B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
   } else if (KIND == kVarM) {
-    const uint32_t tiles_m = (uint32_t)s_start[g.E];
-    const uint32_t tile = tile_i;
+    group_table(g.offsets, g.E, g.M, s_off, s_start);
+    const uint32_t tiles_m = (uint32_t)s_start[g.E];  // data-dependent M-tile count
+    const uint32_t tile = blockIdx.x;
+    if (tile >= tiles_m * g.tiles_n) return;          // surplus workgroup
     uint32_t tm, tn;
     raster<kGroupMVarM>(tile, tiles_m, g.tiles_n, tm, tn);
     int lo = 0, hi = g.E - 1;                         // group e: s_start[e] <= tm < s_start[e+1]
@@ -391,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     // of 64 workgroups (8 per XCD, dispatched round-robin) workgroup
     // 64q + 8r + x takes tile 64q + 8x + r: 8 consecutive tiles, which share
     // an A panel, then run on one XCD and share its L2.
-    uint32_t tile = tile_i;
-    if ((tile | 63u) < ntiles) tile = (tile & ~63u) | ((tile & 7u) << 3) | ((tile >> 3) & 7u);
+    uint32_t tile = blockIdx.x;
+    if ((tile | 63u) < g.nblocks) tile = (tile & ~63u) | ((tile & 7u) << 3) | ((tile >> 3) & 7u);
     const uint32_t tn = tile % g.tiles_n, tmg = tile / g.tiles_n;
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
     const int e = (int)(tmg / tiles_m);
@@ -421,8 +408,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // kdim < 2^31 (the launchers check that a tile's byte offsets fit in 32 bits)
   const uint32_t kdim32 = (uint32_t)kdim;
   const int32_t nsteps = (int32_t)((kdim + TK - 1) / TK);
-  const LaneOffsets oA = lane_offsets(A, t);
-  const LaneOffsets oB = lane_offsets(B, t);
+  const LaneOffsets oA = lane_offsets(A);
+  const LaneOffsets oB = lane_offsets(B);
   const i32x4 none = make_rsrc(g.c, 0);              // zero range: loads read 0
   const uint32_t lds_codes = lds_addr(smem), lds_scales = lds_addr(ssc);
 
@@ -669,26 +656,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
                                   n0 * 2 + col * 16) = v;
       }
     }
-  } else {
+    return;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t ml = wm * 128 + i * 32 + r32;
-      if (ml >= c_rows) continue;
-      const int64_t m = m0 + ml;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ml = wm * 128 + i * 32 + r32;
+    if (ml >= c_rows) continue;
+    const int64_t m = m0 + ml;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + bn + j * 32 + q * 8 + half * 4;
-          store4<OUT>(cbase, g.ldc, m, n, g.N, acc[i][j][4 * q] * mul,
-                      acc[i][j][4 * q + 1] * mul, acc[i][j][4 * q + 2] * mul,
-                      acc[i][j][4 * q + 3] * mul);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + bn + j * 32 + q * 8 + half * 4;
+        store4<OUT>(cbase, g.ldc, m, n, g.N, acc[i][j][4 * q] * mul,
+                    acc[i][j][4 * q + 1] * mul, acc[i][j][4 * q + 2] * mul,
+                    acc[i][j][4 * q + 3] * mul);
       }
     }
-  }
-  // The next tile's loads overwrite the LDS the staged tile was read from.
-  __syncthreads();
   }
 }
 
@@ -713,28 +697,11 @@ static void launch_kernel(const GemmArgs& g, uint32_t blocks, int out, hipStream
 }
 
 // Scale windows need both operands' scale row strides to be multiples of 16.
-static int gemm_num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
-// `tiles`: the output tile count (an upper bound for variable M).  Dense and
-// variable-M grids have one workgroup per CU (at most); variable K keeps one
-// workgroup per tile, so the hardware's dispatcher balances the uneven tiles.
 template <int KIND, bool PT>
-static int launch_gemm(GemmArgs& g, int64_t tiles, int out, hipStream_t stream) {
-  if (tiles == 0) return MXQ_OK;
-  if (tiles > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
-  g.ntiles = (uint32_t)tiles;
-  const int64_t cus = gemm_num_cus();
-  const int64_t blocks = KIND == kVarK || tiles < cus ? tiles : cus;
+static int launch_gemm(GemmArgs& g, int64_t blocks, int out, hipStream_t stream) {
+  if (blocks == 0) return MXQ_OK;
+  if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
+  g.nblocks = (uint32_t)blocks;
   if constexpr (PT)
     launch_kernel<KIND, PT, false>(g, (uint32_t)blocks, out, stream);
   else if (g.ldsa % 16 == 0 && g.ldsb % 16 == 0)
