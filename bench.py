@@ -36,6 +36,7 @@ PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 MX_BYTES_PER_ELT = 2 + 1 + 1 / 32   # BF16 in, E4M3 code + E8M0 per 32 out
 DUAL_BYTES_PER_ELT = 2 + 2 * (1 + 1 / 32)   # BF16 in once, row and column copies out
 HIDDEN, FFN, E, TOKENS, TOP_K = 2048, 1408, 64, 8192, 6
+COPY_CALIBRATION_BYTES = 1 << 30
 
 # kernel-function names as rocprofv3 reports them
 KFN = {
@@ -59,6 +60,9 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize each tensor with separate row-wise and column-wise passes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB device-to-device copy (the known-size reference "
+                         "that scales rocprofv3 FETCH_SIZE/WRITE_SIZE counts to bytes)")
     return ap.parse_args()
 
 
@@ -120,6 +124,14 @@ def main():
     offs_d = torch.from_numpy(offs).to(dev)
     w_off_gu = torch.arange(E + 1, dtype=torch.int64, device=dev) * (2 * FFN)
     w_off_dn = torch.arange(E + 1, dtype=torch.int64, device=dev) * HIDDEN
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     T = Timer(torch)
 

@@ -1,0 +1,143 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+  python -m block_quant_gemm_amd.profsum stats KERNEL_STATS_CSV
+      Markdown table of a `rocprofv3 --kernel-trace --stats` summary
+      (library kernels first; durations in microseconds).
+
+  python -m block_quant_gemm_amd.profsum traffic --fetch DIR --write DIR -o JSON
+      HBM bytes per dispatch of each library kernel from two `rocprofv3 --pmc`
+      runs of `bench.py --copy-calibration` (one with FETCH_SIZE, one with
+      WRITE_SIZE; both counters are KiB per dispatch).  Each counter is scaled
+      by the factor that makes the run's 1 GiB device-to-device copy read and
+      write exactly 1 GiB.  The JSON records the kernel-source digest, so that
+      bench.py reports the figures only while the kernels are unchanged.
+"""
+
+import argparse
+import csv
+import glob
+import json
+import os
+import sys
+from collections import defaultdict
+
+LIB_PREFIX = ("void mxq::", "mxq::")
+COPY_BYTES = 1 << 30
+
+
+def short_name(name):
+    """`void mxq::k_gemm<1, false, 0, true>(mxq::GemmArgs)` -> `k_gemm<1,false,0,true>`."""
+    n = name
+    for p in LIB_PREFIX:
+        if n.startswith(p):
+            n = n[len(p):]
+    depth, out = 0, []
+    for ch in n:
+        if ch == "(" and depth == 0:
+            break
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        out.append(ch)
+    return "".join(out).replace(" ", "")
+
+
+def is_lib(name):
+    return name.startswith(LIB_PREFIX)
+
+
+def stats(path):
+    rows = list(csv.DictReader(open(path, newline="")))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["| kernel | calls | total us | average us | min us | max us | % of GPU time |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    other = [0, 0.0]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        if not is_lib(r["Name"]):
+            other[0] += int(r["Calls"])
+            other[1] += float(r["TotalDurationNs"])
+            continue
+        lines.append("| %s | %s | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["TotalDurationNs"]) / 1e3,
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            100.0 * float(r["TotalDurationNs"]) / total))
+    lines.append("| (other: torch set-up and copies) | %d | %.1f | | | | %.2f |" % (
+        other[0], other[1] / 1e3, 100.0 * other[1] / total))
+    return "\n".join(lines)
+
+
+def _counter_rows(d, counter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    out = []
+    for f in files:
+        for r in csv.DictReader(open(f, newline="")):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def _per_kernel(rows):
+    acc = defaultdict(list)
+    for _, name, v in rows:
+        if is_lib(name):
+            acc[short_name(name)].append(v)
+    return acc
+
+
+def _copy_kib(rows):
+    """KiB the calibration copy reports: the largest copy-kernel dispatch."""
+    vals = [v for _, name, v in rows if "copy" in name.lower() and not is_lib(name)]
+    if not vals:
+        raise SystemExit("no copy-kernel dispatch found (run bench.py --copy-calibration)")
+    return max(vals)
+
+
+def traffic(fetch_dir, write_dir):
+    fr, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (_copy_kib(fr) * 1024.0)
+    w_scale = COPY_BYTES / (_copy_kib(wr) * 1024.0)
+    fk, wk = _per_kernel(fr), _per_kernel(wr)
+    kernels = {}
+    for k in sorted(set(fk) | set(wk)):
+        f = sum(fk.get(k, [0])) / max(len(fk.get(k, [])), 1) * 1024.0 * f_scale
+        w = sum(wk.get(k, [0])) / max(len(wk.get(k, [])), 1) * 1024.0 * w_scale
+        kernels[k] = {"dispatches": max(len(fk.get(k, [])), len(wk.get(k, []))),
+                      "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+                      "hbm_bytes_per_launch": f + w}
+    from block_quant_gemm_amd.build import source_digest
+    return {"what": "HBM bytes per dispatch (average over the run's dispatches of each "
+                    "kernel) from rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB "
+                    "device-to-device copy",
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "source_digest": source_digest(), "kernels": kernels}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("-o", "--out")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats(a.csv))
+    else:
+        rec = traffic(a.fetch, a.write)
+        txt = json.dumps(rec, indent=1)
+        if a.out:
+            with open(a.out, "w") as f:
+                f.write(txt + "\n")
+        print(txt)
+
+
+if __name__ == "__main__":
+    ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    main()

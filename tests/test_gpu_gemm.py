@@ -86,7 +86,8 @@ def _relayout_scales(s, layout):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (200, 136, 96), (129, 257, 160), (64, 40, 1408),
-                                   (3, 500, 2048), (300, 264, 1056)])
+                                   (3, 500, 2048), (300, 264, 1056), (300, 1024, 256),
+                                   (257, 1300, 96)])
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
 def test_dense_ragged(M, N, K, out, layout):
@@ -173,6 +174,8 @@ def _grouped_case(counts, N, K, seed):
     ([0, 0, 257], 96, 64),
     ([5], 32, 32),
     ([128, 128, 0, 1, 127, 129], 136, 1408),
+    ([300, 0, 45, 513], 768, 192),
+    ([300, 0, 45, 513], 700, 128),
 ])
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
@@ -238,6 +241,8 @@ def test_grouped_moe_gate_up_sampled():
     ([0, 64], 32, 32),
     ([333, 12, 0, 77], 136, 200),
     ([700, 33, 1100, 0, 517], 288, 160),
+    ([300, 0, 45, 513], 296, 768),
+    ([300, 0, 45, 513], 264, 600),
 ])
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
