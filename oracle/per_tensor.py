@@ -41,3 +41,40 @@ def pt_quantize(x_bf16_bits):
 def pt_dequantize(codes, scale):
     """Exact float64 values q * scale."""
     return e4m3_decode(codes) * np.float64(np.float32(scale))
+
+
+def pg_quantize(x_bf16_bits, offsets):
+    """Per-group current scaling of a 2-D BF16 tensor whose rows are grouped
+    by expert: rows [offsets[e], offsets[e+1]) share one FP32 scale, found by
+    the per-tensor rule above from that group's own amax.
+
+    [HP329] §3 (format table: HiF8 current scaling keeps one FP32 scale per
+    dense tensor and, for grouped tensors, one per leading group) and §3.2
+    (``scale = valid(amax) ? amax / format_max : 1.0``; 3-D grouped weights
+    use a per-leading-group scale); [TTNPU] MoE expert layers (each expert
+    group shares one scale).  Reading: the groups of a [M, K] activation are
+    its expert row ranges; a 3-D weight [E, N, K] is the same with offsets
+    e * N; an empty group gets 1.0.
+
+    Returns (codes uint8 [M, K], scales float32 [E])."""
+    bits = np.asarray(x_bf16_bits, dtype=np.uint16)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = offsets.size - 1
+    codes = np.zeros(bits.shape, dtype=np.uint8)
+    scales = np.ones(E, dtype=np.float32)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            codes[lo:hi], scales[e] = pt_quantize(bits[lo:hi])
+    return codes, scales
+
+
+def pg_dequantize(codes, scales, offsets):
+    """Exact float64 values: row r of group e is codes[r] * scales[e]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    out = np.zeros(np.shape(codes), dtype=np.float64)
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[lo:hi] = pt_dequantize(codes[lo:hi], scales[e])
+    return out

@@ -77,3 +77,103 @@ def test_dequant_error_relative():
     # two roundings: FP32 quotient (relative 2^-24) then E4M3 (half a step)
     bound = (step / 2 + a * 2.0 ** -23) * np.float64(s)
     assert np.all(np.abs(d - v) <= bound)
+
+
+# ---------------------------------------------------------------------------
+# per-group (per-expert) current scaling: [HP329] §3 and §3.2, one FP32 scale
+# per leading group
+# ---------------------------------------------------------------------------
+
+def _groups(counts):
+    counts = np.asarray(counts, np.int64)
+    return workloads.offsets_from_counts(counts)
+
+
+def test_per_group_scales_closed_form_and_empty_groups():
+    """Each group's scale is its own amax / 448 (hand-picked amaxes whose
+    quotients are exact), an empty group gets 1.0 ([HP329] §3.2 'valid(amax)
+    ? amax / format_max : 1.0')."""
+    offs = _groups([2, 0, 3, 1])
+    x = bf16([[1.0, -3.5], [0.5, 2.0],                  # group 0: amax 3.5
+              [-896.0, 1.0], [7.0, 0.0], [0.25, 448.0],  # group 2: amax 896
+              [0.0, -0.0]])                             # group 3: amax 0
+    codes, s = per_tensor.pg_quantize(x, offs)
+    assert s.dtype == np.float32
+    assert s.tolist() == [0.0078125, 1.0, 2.0, 1.0]
+    # 3.5 / 0.0078125 = 448 -> 0x7E with its sign; 896 / 2 = 448
+    assert codes[0, 1] == 0xFE and codes[2, 0] == 0xFE
+    assert codes[4, 1] == 0x76            # 448 / 2 = 224 = 1.75 * 2^7: exponent field 14, mantissa 6
+    assert codes[5].tolist() == [0x00, 0x80]             # signed zeros kept
+
+
+def test_per_group_amax_elements_map_to_448():
+    counts = [300, 1, 0, 77, 512]
+    offs = _groups(counts)
+    x = workloads.bf16_normal((sum(counts), 96), 1.0, seed=11, name="pg",
+                              outlier_frac=0.01, outlier_scale=50.0)
+    codes, s = per_tensor.pg_quantize(x, offs)
+    v = codec.bf16_bits_to_f64(x)
+    for e in range(len(counts)):
+        lo, hi = offs[e], offs[e + 1]
+        if hi == lo:
+            assert s[e] == 1.0
+            continue
+        blk = np.abs(v[lo:hi])
+        r, c = np.unravel_index(np.argmax(blk), blk.shape)
+        assert codes[lo + r, c] & 0x7F == 0x7E
+        assert np.all((codes[lo:hi] & 0x7F) <= 0x7E)
+
+
+def test_per_group_matches_torch_division_and_cast():
+    """Independent route per group: torch amax, FP32 division, e4m3fn cast."""
+    counts = [129, 0, 31, 250]
+    offs = _groups(counts)
+    x = workloads.bf16_normal((sum(counts), 64), 0.02, seed=12, name="pg2",
+                              outlier_frac=0.005, outlier_scale=50.0)
+    codes, s = per_tensor.pg_quantize(x, offs)
+    xt = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float()
+    for e in range(len(counts)):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi == lo:
+            continue
+        amax = xt[lo:hi].abs().max()
+        se = amax / torch.tensor(448.0)
+        assert np.float32(se.item()) == s[e]
+        ref = (xt[lo:hi] / se).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(codes[lo:hi], ref.numpy())
+
+
+def test_per_group_equivariance_and_isolation():
+    """Scaling one group by 2^j scales only its scale and leaves every code
+    unchanged; a NaN in one group affects that group only."""
+    counts = [40, 60, 25]
+    offs = _groups(counts)
+    x = workloads.bf16_normal((sum(counts), 32), 1.0, seed=13, name="pg3")
+    c0, s0 = per_tensor.pg_quantize(x, offs)
+    v = codec.bf16_bits_to_f64(x)
+    v2 = v.copy()
+    v2[offs[1]:offs[2]] *= 2.0 ** -7
+    c1, s1 = per_tensor.pg_quantize(bf16(v2), offs)
+    assert np.array_equal(c0, c1)
+    assert s1[0] == s0[0] and s1[2] == s0[2]
+    assert s1[1] == np.float32(s0[1] * np.float32(2.0 ** -7))
+    xn = x.copy()
+    xn[offs[2] + 3, 5] = 0x7FC0                           # NaN in group 2
+    c2, s2 = per_tensor.pg_quantize(xn, offs)
+    assert s2[2] == 1.0 and s2[0] == s0[0] and s2[1] == s0[1]
+    assert np.array_equal(c2[:offs[2]], c0[:offs[2]])
+    assert c2[offs[2] + 3, 5] == 0x7F
+
+
+def test_per_group_dequantize_exact():
+    counts = [3, 0, 2]
+    offs = _groups(counts)
+    codes = np.array([[0x38, 0xC0], [0x7E, 0x00], [0x01, 0x80],
+                      [0x30, 0x48], [0xB8, 0x08]], np.uint8)
+    s = np.array([0.5, 3.0, 2.0 ** -3], np.float32)
+    d = per_tensor.pg_dequantize(codes, s, offs)
+    # E4M3: 0x38 = 1, 0xC0 = -2, 0x7E = 448, 0x01 = 2^-9, 0x30 = 0.5, 0x48 = 4,
+    # 0xB8 = -1, 0x08 = 2^-6
+    exp = np.array([[0.5, -1.0], [224.0, 0.0], [2.0 ** -10, -0.0],
+                    [2.0 ** -4, 0.5], [-(2.0 ** -3), 2.0 ** -9]])
+    assert np.array_equal(d, exp)
