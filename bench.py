@@ -260,6 +260,8 @@ def main():
                   "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
     if not args.no_dense:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
+    components["moe_gate_up_per_expert_scaling"] = per_group_component(
+        torch, mxq, X, Wgu, offs_d, w_off_gu, M)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -345,6 +347,36 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "per_tensor_quant_X": {"us": t_px * 1e3, "GB_per_s_algorithmic": gb(nX, 3, t_px)},
         "per_tensor_quant_W": {"us": t_pw * 1e3, "GB_per_s_algorithmic": gb(nW, 3, t_pw)},
         "per_tensor_gemm_fwd": {"us": t_pg * 1e3, "TFLOP_per_s": flops / (t_pg * 1e-3) / 1e12},
+    }
+
+
+def per_group_component(torch, mxq, X, Wgu, offs_d, w_off_gu, M, reps=5):
+    """Second format on the MoE gate/up forward: per-expert current scaling
+    (one FP32 scale per expert group of X rows and per expert weight) and the
+    grouped GEMM with per-group scales."""
+    def timed(fn, *a):
+        for _ in range(2):
+            r = fn(*a)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            r = fn(*a)
+        e.record()
+        torch.cuda.synchronize()
+        return r, s.elapsed_time(e) / reps
+
+    (xq, xs), t_qx = timed(mxq.fp8_quantize_per_group, X, offs_d)
+    (wq, ws), t_qw = timed(mxq.fp8_quantize_per_group, Wgu, w_off_gu)
+    _, t_g = timed(mxq.fp8_grouped_gemm_per_group, xq, xs, wq.view(E, 2 * FFN, HIDDEN), ws,
+                   offs_d)
+    flops = 2 * M * 2 * FFN * HIDDEN
+    gb = lambda n, ms: n * 3 / (ms * 1e-3) / 1e9
+    return {
+        "quant_X": {"us": t_qx * 1e3, "GB_per_s_algorithmic": gb(X.numel(), t_qx)},
+        "quant_W_gu": {"us": t_qw * 1e3, "GB_per_s_algorithmic": gb(Wgu.numel(), t_qw)},
+        "grouped_gemm": {"us": t_g * 1e3, "TFLOP_per_s": flops / (t_g * 1e-3) / 1e12},
     }
 
 

@@ -116,7 +116,7 @@ struct GemmArgs {
   const uint8_t* a; const uint8_t* as; int64_t lda, ldsa;
   const uint8_t* b; const uint8_t* bs; int64_t ldb, ldsb;
   int64_t b_estride, bs_estride;                    // per-group B strides (variable M)
-  const float* pta; const float* ptb;               // per-tensor scales
+  const float* pta; const float* ptb;               // per-tensor scales (variable M: per group)
   const int64_t* offsets; int32_t E;
   int64_t M, N, K;
   void* c; int64_t ldc;
@@ -342,6 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // ---- map the workgroup to (group, m0, n0) ----
   int64_t m0 = 0, n0 = 0, kdim = g.K, c_rows = 0;
   void* cbase = g.c;
+  int group = 0;                                    // the tile's group (variable M, K)
   OpTile A, B;
   if (KIND == kDense) {
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
@@ -365,12 +366,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
       if (s_start[mid] <= (int32_t)tm) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
+    group = e;
     m0 = s_off[e] + (int64_t)(tm - s_start[e]) * TM;
     n0 = (int64_t)tn * TN;
     c_rows = s_off[e + 1] - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, true, SW);
-    B = op_tile(g.b + (int64_t)e * g.b_estride, g.bs + (int64_t)e * g.bs_estride, g.ldb, g.ldsb,
-                n0, 0, g.N - n0, kdim, true, SW);
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
+    B = op_tile(g.b + (int64_t)e * g.b_estride, PT ? nullptr : g.bs + (int64_t)e * g.bs_estride,
+                g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
   } else {
     // variable K: tile = (e, tm over rows of A = dW rows, tn over rows of B =
     // dW cols).  Work per tile is proportional to the group's tokens, so the
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // ---- epilogue: acc[i][j] holds C[m = wm*128 + i*32 + lane%32]
   //                [n = bn + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
   float mul = 1.0f;
-  if (PT) mul = (*g.pta) * (*g.ptb);
+  if (PT) mul = g.pta[group] * g.ptb[group];
   const bool staged = OUT == MXQ_OUT_BF16 && n0 + TN <= g.N && (g.ldc & 7) == 0 &&
                       (reinterpret_cast<uintptr_t>(cbase) & 15) == 0;
   if (staged) {
@@ -807,6 +809,33 @@ extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t
   g.offsets = offsets; g.E = E;
   const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
   return launch_gemm<kVarM, false>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
+}
+
+extern "C" int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scales, int64_t lda,
+                                          const uint8_t* b, const float* b_scales, int64_t ldb,
+                                          int64_t b_estride, const int64_t* offsets, int32_t E,
+                                          int64_t M, int64_t N, int64_t K, void* c, int64_t ldc,
+                                          int out_dtype, int accum, hipStream_t stream) {
+  int st = check_common(M, N, K, ldc, out_dtype, accum);
+  if (st) return st;
+  if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets || !a_scales || !b_scales) return MXQ_ERR_NULL;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!c) return MXQ_ERR_NULL;
+  if (K % 32 != 0) return MXQ_ERR_SHAPE;
+  if (K > 0) {
+    if ((st = check_operand(a, a_scales, lda, 0, K, false))) return st;
+    if ((st = check_operand(b, b_scales, ldb, 0, K, false))) return st;
+  }
+  if (b_estride < 0) return MXQ_ERR_SHAPE;
+  if (b_estride % 16 != 0) return MXQ_ERR_ALIGN;
+  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
+  GemmArgs g = make_args(a, nullptr, lda, 0, b, nullptr, ldb, 0, M, N, K, c, ldc);
+  g.b_estride = b_estride;
+  g.pta = a_scales; g.ptb = b_scales;
+  g.offsets = offsets; g.E = E;
+  const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
+  return launch_gemm<kVarM, true>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
 }
 
 extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t,

@@ -446,6 +446,121 @@ __global__ void k_fill_f32(float* p, float v) {
   if (threadIdx.x == 0) *p = v;
 }
 
+__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-group (per-expert) current scaling: rows [offsets[e], offsets[e+1])
+// share one FP32 scale.  Pass 1 takes each row's packed |x| maximum (one
+// wavefront per row, 16-byte loads, four in flight per lane), pass 2 reduces
+// each group's rows to its amax and scale (one workgroup per group, so an
+// empty group gets 1.0), pass 3 encodes every row with its group's scale
+// exactly as the per-tensor pass does.
+// ---------------------------------------------------------------------------
+
+constexpr int kPgThreads = 256;
+constexpr int kPgMaxGroups = 256;
+
+__global__ __launch_bounds__(kPgThreads) void k_pg_rowmax(const uint16_t* __restrict__ x,
+                                                          int64_t M, int64_t K, int64_t ldx,
+                                                          uint32_t* __restrict__ rowmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kPgThreads / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (kPgThreads / 64) + (threadIdx.x >> 6); r < M;
+       r += nw) {
+    const uint16_t* row = x + r * ldx;
+    uint32_t m = 0;
+    for (int64_t c0 = lane * 8; c0 < K; c0 += 4 * 512) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = c0 + u * 512 < K ? *reinterpret_cast<const uint4*>(row + c0 + u * 512)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u16x2 mm = __builtin_elementwise_max(absmax2(v[u].x, v[u].y), absmax2(v[u].z, v[u].w));
+        const uint32_t t = mm.x > mm.y ? mm.x : mm.y;
+        m = m > t ? m : t;
+      }
+    }
+    for (int sh = 32; sh >= 1; sh >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)m, sh, 64);
+      m = m > o ? m : o;
+    }
+    if (lane == 0) rowmax[r] = m;
+  }
+}
+
+__global__ __launch_bounds__(kPgThreads) void k_pg_scale(const uint32_t* __restrict__ rowmax,
+                                                         const int64_t* __restrict__ offsets,
+                                                         int64_t M, uint32_t* __restrict__ gmax,
+                                                         float* __restrict__ scales) {
+  __shared__ uint32_t red[kPgThreads / 64];
+  const int e = blockIdx.x;
+  int64_t lo = offsets[e], hi = offsets[e + 1];
+  lo = lo < 0 ? 0 : (lo > M ? M : lo);
+  hi = hi < lo ? lo : (hi > M ? M : hi);
+  uint32_t m = 0;
+  for (int64_t r = lo + threadIdx.x; r < hi; r += blockDim.x) m = m > rowmax[r] ? m : rowmax[r];
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) {
+    float sc = 1.0f;
+    if (m < 0x7F80u && m != 0u) sc = __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f);
+    scales[e] = sc;
+    gmax[e] = m;
+  }
+}
+
+__global__ __launch_bounds__(kPgThreads) void k_pg_quant(const uint16_t* __restrict__ x,
+                                                         int64_t M, int64_t K, int64_t ldx,
+                                                         const int64_t* __restrict__ offsets,
+                                                         int32_t E, const uint32_t* __restrict__ gmax,
+                                                         const float* __restrict__ scales,
+                                                         uint8_t* __restrict__ q, int64_t ldq) {
+  __shared__ int64_t s_off[kPgMaxGroups + 1];
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = offsets[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (kPgThreads / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (kPgThreads / 64) + (threadIdx.x >> 6); r < M;
+       r += nw) {
+    // group of row r: the last e with offsets[e] <= r (empty groups skipped)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const bool nonfinite = gmax[lo] >= 0x7F80u;
+    const float sc = scales[lo];
+    const bool direct = sc < 1.17549435e-38f;     // subnormal scale: divide directly
+    const float rc = __frcp_rn(sc);
+    const uint16_t* row = x + r * ldx;
+    uint8_t* qrow = q + r * ldq;
+    for (int64_t c = lane * 8; c < K; c += 512) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + c);
+      uint32_t lo32, hi32;
+      if (nonfinite) {
+        lo32 = pt_nonfinite_pair<false>(v.x, 0u);
+        lo32 = pt_nonfinite_pair<true>(v.y, lo32);
+        hi32 = pt_nonfinite_pair<false>(v.z, 0u);
+        hi32 = pt_nonfinite_pair<true>(v.w, hi32);
+      } else {
+        lo32 = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.x), sc, rc, direct),
+                                    pt_div(bf16_hi(v.x), sc, rc, direct), 0u);
+        lo32 = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.y), sc, rc, direct),
+                                   pt_div(bf16_hi(v.y), sc, rc, direct), lo32);
+        hi32 = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.z), sc, rc, direct),
+                                    pt_div(bf16_hi(v.z), sc, rc, direct), 0u);
+        hi32 = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.w), sc, rc, direct),
+                                   pt_div(bf16_hi(v.w), sc, rc, direct), hi32);
+      }
+      *reinterpret_cast<uint2*>(qrow + c) = make_uint2(lo32, hi32);
+    }
+  }
+}
+
 }  // namespace mxq
 
 // ---------------------------------------------------------------------------
@@ -547,9 +662,51 @@ extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t
   return launch_status();
 }
 
-extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t, int64_t, int64_t) {
+extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t a1, int64_t, int64_t) {
   if (op == MXQ_WS_PER_TENSOR) return n > 0 ? kPtBlocks * sizeof(uint32_t) : 0;
+  if (op == MXQ_WS_PER_GROUP)                        // n = rows, a1 = groups
+    return n >= 0 && a1 > 0 ? (size_t)(n + a1) * sizeof(uint32_t) : 0;
   return 0;
+}
+
+extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const int64_t* offsets, int32_t E, uint8_t* q,
+                                      int64_t ldq, float* scales, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
+  if (M > 0 && K > 0 && (!x || !q)) return MXQ_ERR_NULL;
+  if (K % 8 != 0) return MXQ_ERR_SHAPE;
+  if (M > 0 && K > 0) {                              // strides of empty inputs are not used
+    if (ldx < K || ldq < K) return MXQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || ldq % 8 != 0 || !aligned(x, 16) || !aligned(q, 8)) return MXQ_ERR_ALIGN;
+  }
+  if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
+    return MXQ_ERR_WORKSPACE;
+  uint32_t* rowmax = static_cast<uint32_t*>(workspace);
+  uint32_t* gmax = rowmax + M;
+  const int64_t waves = (int64_t)num_cus() * 64;    // rows in flight: 16 wavefronts per CU
+  const int64_t rows_blocks = (M + 3) / 4;
+  const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
+                                                             : waves / 4);
+  if (M > 0 && K > 0) {
+    hipLaunchKernelGGL(k_pg_rowmax, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
+                       rowmax);
+  } else if (M > 0) {
+    hipLaunchKernelGGL(k_fill_u32, dim3((uint32_t)((M + 255) / 256)), dim3(256), 0, stream,
+                       rowmax, M, 0u);
+  }
+  int st = launch_status();
+  if (st != MXQ_OK) return st;
+  hipLaunchKernelGGL(k_pg_scale, dim3((uint32_t)E), dim3(kPgThreads), 0, stream, rowmax, offsets,
+                     M, gmax, scales);
+  st = launch_status();
+  if (st != MXQ_OK || M == 0 || K == 0) return st;
+  hipLaunchKernelGGL(k_pg_quant, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
+                     offsets, E, gmax, scales, q, ldq);
+  return launch_status();
 }
 
 extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,

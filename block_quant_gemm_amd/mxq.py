@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 OUT_BF16, OUT_FP32 = 0, 1
 ACC_MFMA_FP8, ACC_FP32 = 0, 1
-WS_PER_TENSOR = 0
+WS_PER_TENSOR, WS_PER_GROUP = 0, 1
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 
@@ -30,6 +30,8 @@ _SIGS = {
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _i64,
                                         _p, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_quantize_per_tensor": (ctypes.c_int, [_p, _i64, _p, _p, _p, _sz, _p]),
+    "fp8_quantize_per_group": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p,
+                                              _p, _sz, _p]),
     "mx_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64,
                                _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
     "fp8_gemm_per_tensor": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
@@ -37,6 +39,9 @@ _SIGS = {
     "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _i32,
                                        _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                        ctypes.c_int, _p]),
+    "fp8_grouped_gemm_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i32,
+                                                  _i64, _i64, _i64, _p, _i64, ctypes.c_int,
+                                                  ctypes.c_int, _p]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _p,
                                              _i32, _i64, _i64, _p, _i64, ctypes.c_int,
                                              ctypes.c_int, _p]),
@@ -199,6 +204,26 @@ def fp8_quantize_per_tensor(x, q=None, scale=None, workspace=None):
     return q, scale
 
 
+def fp8_quantize_per_group(x, offsets, q=None, scales=None, workspace=None):
+    """Per-group (per-expert) current-scaling E4M3 of a BF16 [M, K] matrix
+    whose rows [offsets[e], offsets[e+1]) form group e (offsets int64 [E+1]
+    on the device).  Returns (codes uint8 [M, K], scales float32 [E])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = offsets.numel() - 1
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(E, dtype=torch.float32, device=x.device)
+    ws = workspace_size(WS_PER_GROUP, M, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=x.device)
+    _check(load().fp8_quantize_per_group(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q),
+                                         q.stride(0), _ptr(scales), _ptr(workspace),
+                                         workspace.numel(), _stream()))
+    return q, scales
+
+
 # ---------------------------------------------------------------------------
 # GEMMs
 # ---------------------------------------------------------------------------
@@ -247,6 +272,21 @@ def mx_grouped_gemm(a, a_scale, b, b_scale, offsets, out_dtype=OUT_BF16,
                                   _ptr(b), _ptr(b_scale), b.stride(1), b_scale.stride(1),
                                   b.stride(0), b_scale.stride(0), _ptr(offsets), E, M, N, K,
                                   _ptr(c), c.stride(0), out_dtype, accum, _stream()))
+    return c
+
+
+def fp8_grouped_gemm_per_group(a, a_scales, b, b_scales, offsets, out_dtype=OUT_BF16,
+                               accum=ACC_MFMA_FP8, c=None):
+    """Variable-M grouped GEMM with per-group FP32 scales: rows [o_e, o_e+1)
+    of C are a_scales[e] * b_scales[e] * (Q_a[rows] · Q_b[e]ᵀ).  a [M, K] and
+    b [E, N, K] codes from fp8_quantize_per_group; scales float32 [E]."""
+    M, K = a.shape
+    E, N, _ = b.shape
+    c = _out(M, N, out_dtype, a.device, c)
+    _check(load().fp8_grouped_gemm_per_group(_ptr(a), _ptr(a_scales), a.stride(0), _ptr(b),
+                                             _ptr(b_scales), b.stride(1), b.stride(0),
+                                             _ptr(offsets), E, M, N, K, _ptr(c), c.stride(0),
+                                             out_dtype, accum, _stream()))
     return c
 
 

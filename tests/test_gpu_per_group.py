@@ -1,0 +1,192 @@
+"""Parity of the HIP per-group (per-expert) current-scaling quantizer and of
+the grouped FP8 GEMM with per-group scales against the oracle, through the C
+ABI.  Codes and scales must be bit-exact; GEMM outputs within the tolerance
+of oracle.gemm (1e-5 * S + 1e-6 plus the FP8 matrix-unit allowance)."""
+
+import numpy as np
+import pytest
+import torch
+
+from block_quant_gemm_amd import mxq, workloads
+from oracle import codec, gemm, per_tensor
+from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant(bits, offs):
+    q, s = mxq.fp8_quantize_per_group(to_dev_bf16(bits), to_dev(offs))
+    return q, s, host(q), host(s)
+
+
+def _assert_quant_equal(bits, offs, qh, sh):
+    rq, rs = per_tensor.pg_quantize(bits, offs)
+    assert np.array_equal(sh.view(np.uint32), rs.view(np.uint32)), (sh, rs)
+    if not np.array_equal(qh, rq):
+        bad = np.argwhere(qh != rq)[:8]
+        raise AssertionError(f"codes differ at {bad.tolist()}: "
+                             f"{qh[tuple(bad.T)].tolist()} vs {rq[tuple(bad.T)].tolist()}")
+
+
+@pytest.mark.parametrize("counts,K", [
+    ([40, 0, 1, 130, 0, 300, 0], 64),
+    ([0, 0, 257], 136),
+    ([5], 8),
+    ([1000, 17, 0, 2, 511], 2048),
+    ([0], 32),
+])
+def test_per_group_quant_bit_exact(counts, K):
+    say(f"per-group quant counts={counts} K={K}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    x = workloads.bf16_normal((int(counts.sum()), K), 1.0, seed=K, name="pgx",
+                              outlier_frac=0.01, outlier_scale=100.0)
+    _, _, qh, sh = _quant(x, offs)
+    _assert_quant_equal(x, offs, qh, sh)
+
+
+def test_per_group_quant_special_groups():
+    """NaN, Inf, all-zero, subnormal-scale, amax = 448 (s = 1) and empty
+    groups side by side; a group's special values affect that group only."""
+    say("per-group quant special groups")
+    counts = np.array([8, 8, 8, 0, 8, 8, 8], np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    K = 64
+    x = workloads.bf16_normal((48, K), 1.0, seed=3, name="pgs")
+    x[offs[0] + 2, 7] = 0x7FC0                       # NaN in group 0
+    x[offs[1] + 5, 1] = 0xFF80                       # -Inf in group 1
+    x[offs[2]:offs[3]] = 0                           # zeros in group 2 (+0 and -0)
+    x[offs[2] + 1, ::2] = 0x8000
+    tiny = workloads.bf16_normal((8, K), 1.0, seed=4, name="pgt")
+    v = codec.bf16_bits_to_f64(tiny) * 2.0 ** -122   # amax / 448 is FP32-subnormal
+    t32 = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16)
+    x[offs[4]:offs[5]] = t32.view(torch.int16).numpy().view(np.uint16)
+    x[offs[5] + 3, 9] = 0x43E0                       # 448 in group 5
+    x[offs[5]:offs[6]] &= 0xBFFF                     # keep the rest small: |v| < 2
+    x[offs[5] + 3, 9] = 0x43E0
+    _, _, qh, sh = _quant(x, offs)
+    _assert_quant_equal(x, offs, qh, sh)
+    assert sh[0] == 1.0 and sh[1] == 1.0 and sh[2] == 1.0 and sh[3] == 1.0
+    assert sh[4] < np.float32(1.17549435e-38)
+    assert sh[5] == 1.0
+
+
+def test_per_group_quant_strided_and_weights():
+    """Row strides beyond K and a 3-D weight stack with offsets e*N."""
+    say("per-group quant strided / weight stack")
+    E, N, K = 6, 96, 160
+    w = workloads.bf16_normal((E * N, K), 0.02, seed=5, name="pgw")
+    offs = np.arange(E + 1, dtype=np.int64) * N
+    xs = torch.zeros((E * N, K + 24), dtype=torch.bfloat16, device="cuda")
+    xs[:, :K] = to_dev_bf16(w)
+    q = torch.full((E * N, K + 16), 0xA5, dtype=torch.uint8, device="cuda")
+    qv, sc = mxq.fp8_quantize_per_group(xs[:, :K], to_dev(offs), q=q[:, :K])
+    torch.cuda.synchronize()
+    _assert_quant_equal(w, offs, host(qv), host(sc))
+    assert torch.all(q[:, K:] == 0xA5)
+
+
+def test_per_group_quant_full_size_moe():
+    """X [49152, 2048] over the 64 Zipf expert groups and W_gu [64*2816, 2048]
+    per expert, bit-exact against the oracle."""
+    say("per-group quant X 49152x2048 and W_gu 180224x2048")
+    d = workloads.moe_forward(0)
+    offs = d["offsets"]
+    _, _, qh, sh = _quant(d["X"], offs)
+    _assert_quant_equal(d["X"], offs, qh, sh)
+    w = d["W_gu"].reshape(64 * 2816, 2048)
+    woffs = np.arange(65, dtype=np.int64) * 2816
+    _, _, qh, sh = _quant(w, woffs)
+    _assert_quant_equal(w, woffs, qh, sh)
+
+
+def _gemm_allowance(ah, bh, sa, sb, offs, N):
+    """MFMA allowance (unit block scales) times the group's two scales, plus
+    the two FP32 roundings of multiplying the scales into the sum."""
+    E = len(offs) - 1
+    K = ah.shape[1]
+    T = np.zeros((ah.shape[0], N))
+    ones_a = np.full((ah.shape[0], K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            T[lo:hi] = gemm.fp8_mfma_truncation_bound(
+                ah[lo:hi], ones_a[lo:hi], bh[e * N:(e + 1) * N], ones_b) * \
+                float(sa[e]) * float(sb[e])
+    return T
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([40, 0, 1, 130, 0, 300, 0], 160, 256),
+    ([300, 0, 45, 513], 768, 192),
+    ([5], 32, 32),
+])
+@pytest.mark.parametrize("out", [mxq.OUT_BF16, mxq.OUT_FP32])
+def test_per_group_grouped_gemm(counts, N, K, out):
+    say(f"per-group grouped gemm counts={counts} N={N} K={K} out={out}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    E, M = len(counts), int(counts.sum())
+    a = workloads.bf16_normal((M, K), 1.0, seed=M + K, name="pga", outlier_frac=0.005,
+                              outlier_scale=50.0)
+    w = workloads.bf16_normal((E * N, K), 0.02, seed=N + K, name="pgb")
+    woffs = np.arange(E + 1, dtype=np.int64) * N
+    aq, sa, ah, sah = _quant(a, offs)
+    wq, sw, wh, swh = _quant(w, woffs)
+    c = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(E, N, K), sw, to_dev(offs),
+                                       out_dtype=out)
+    A = per_tensor.pg_dequantize(ah, sah, offs)
+    B = per_tensor.pg_dequantize(wh, swh, woffs).reshape(E, N, K)
+    Y, S = gemm.grouped_gemm_ref(A, B, offs)
+    T = _gemm_allowance(ah, wh, sah, swh, offs, N) + 2.0 ** -23 * np.abs(Y)
+    if out == mxq.OUT_FP32:
+        ok = gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T)
+    else:
+        ok = gemm.check_bf16_extra(host(c), Y, S, T)
+    say(f"  elements {ok.size}: within tolerance {ok.mean():.6f}")
+    assert ok.all()
+
+
+def test_per_group_one_group_equals_per_tensor():
+    """One group spanning all rows is the per-tensor recipe: same codes,
+    same scale, same GEMM output bit for bit."""
+    say("per-group with one group == per-tensor")
+    a = workloads.bf16_normal((300, 256), 1.0, seed=9, name="pgo")
+    w = workloads.bf16_normal((72, 256), 0.02, seed=9, name="pgw2")
+    one = to_dev(np.array([0, 300], np.int64))
+    aq, sa = mxq.fp8_quantize_per_group(to_dev_bf16(a), one)
+    wq, sw = mxq.fp8_quantize_per_group(to_dev_bf16(w), to_dev(np.array([0, 72], np.int64)))
+    pq, ps = mxq.fp8_quantize_per_tensor(to_dev_bf16(a))
+    assert torch.equal(aq, pq) and torch.equal(sa, ps)
+    cg = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(1, 72, 256), sw, one,
+                                        out_dtype=mxq.OUT_FP32)
+    cd = mxq.fp8_gemm_per_tensor(aq, sa, wq, sw, out_dtype=mxq.OUT_FP32)
+    assert torch.equal(cg, cd)
+
+
+def test_per_group_gate_up_full_size_sampled():
+    """MoE gate_up forward at full size with per-expert scales: 49152 rows,
+    64 experts, W_gu [64, 2816, 2048]; 2000 sampled outputs."""
+    say("per-group grouped gate_up 49152 x 2816 x 2048")
+    d = workloads.moe_forward(0)
+    offs, E = d["offsets"], 64
+    w = d["W_gu"].reshape(E * 2816, 2048)
+    woffs = np.arange(E + 1, dtype=np.int64) * 2816
+    aq, sa, ah, sah = _quant(d["X"], offs)
+    wq, sw, wh, swh = _quant(w, woffs)
+    c = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(E, 2816, 2048), sw, to_dev(offs))
+    rng = np.random.default_rng(2)
+    rows = rng.integers(0, 49152, 2000)
+    n = rng.integers(0, 2816, 2000)
+    e = np.searchsorted(offs, rows, side="right") - 1
+    cols = e * 2816 + n
+    idx = np.arange(len(rows))
+    A = per_tensor.pt_dequantize(ah[rows], np.float32(1.0)) * sah[e].astype(np.float64)[:, None]
+    B = per_tensor.pt_dequantize(wh[cols], np.float32(1.0)) * swh[e].astype(np.float64)[:, None]
+    Y, S = gemm.gemm_ref_entries(A, B, idx, idx)
+    ones = np.full((len(rows), 64), 127, np.uint8)
+    T = gemm.fp8_mfma_truncation_bound(ah[rows], ones, wh[cols], ones, idx, idx) * \
+        sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y)
+    ch = host(c)[rows, n]
+    assert gemm.check_bf16_extra(ch, Y, S, T).all()

@@ -65,3 +65,27 @@ def test_host_validation_errors(lib):
     assert lib.mxq_workspace_size(0, 100, 0, 0, 0) > 0
     assert lib.mxq_workspace_size(0, 0, 0, 0, 0) == 0
     assert lib.mxq_validate_offsets(None, 4, 10, None) == 1
+
+
+def test_per_group_validation_errors(lib):
+    P = 4096
+    # fp8_quantize_per_group(x, M, K, ldx, offsets, E, q, ldq, scales, ws, ws_bytes, stream)
+    ws = lib.mxq_workspace_size(1, 64, 4, 0, 0)
+    assert ws == (64 + 4) * 4
+    assert lib.fp8_quantize_per_group(P, -1, 32, 32, P, 4, P, 32, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, P, 0, P, 32, P, P, ws, None) == 2   # E
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, P, 257, P, 32, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, None, 4, P, 32, P, P, ws, None) == 1
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, P, 4, P, 32, None, P, ws, None) == 1
+    assert lib.fp8_quantize_per_group(P, 64, 36, 40, P, 4, P, 48, P, P, ws, None) == 2   # K % 8
+    assert lib.fp8_quantize_per_group(P, 64, 32, 36, P, 4, P, 32, P, P, ws, None) == 3   # ldx % 8
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, P, 4, P, 36, P, P, ws, None) == 3   # ldq % 8
+    assert lib.fp8_quantize_per_group(P, 64, 32, 32, P, 4, P, 32, P, P, ws - 4, None) == 5
+    # fp8_grouped_gemm_per_group(a, sa, lda, b, sb, ldb, b_estride, offsets, E, M, N, K, c, ldc,
+    #                            out, accum, stream)
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, None, 4, 8, 8, 32, P, 8, 0, 0, None) == 1
+    assert lib.fp8_grouped_gemm_per_group(P, None, 32, P, P, 32, 256, P, 4, 8, 8, 32, P, 8, 0, 0, None) == 1
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 0, 8, 8, 32, P, 8, 0, 0, None) == 2
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 250, P, 4, 8, 8, 32, P, 8, 0, 0, None) == 3
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 40, P, 8, 0, 0, None) == 2
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 32, P, 8, 0, 1, None) == 4
