@@ -128,6 +128,9 @@ def moe_backward(seed=0, tokens=8192, top_k=TOP_K, n_experts=N_EXPERTS):
     }
 
 
+# Tokens of the full block step: sequence 4096 x batch 4.
+BLOCK_TOKENS = 4096 * 4
+
 # MLA projection and shared-expert Linears of one 16B block:
 # (name, in_features, out_features).
 BLOCK_DENSE_LINEARS = [
@@ -139,3 +142,13 @@ BLOCK_DENSE_LINEARS = [
     ("shared_up", HIDDEN, N_SHARED * MOE_FFN),
     ("shared_down", N_SHARED * MOE_FFN, HIDDEN),
 ]
+
+
+def block_linear(name, in_features, out_features, seed=0, tokens=BLOCK_TOKENS):
+    """One dense Linear of the full block step: X [tokens, in] N(0,1), W [out,
+    in] N(0, 0.02), dY [tokens, out] N(0, 1e-3)."""
+    return {
+        "X": bf16_normal((tokens, in_features), 1.0, seed=seed, name=f"blk.{name}.X"),
+        "W": bf16_normal((out_features, in_features), 0.02, seed=seed, name=f"blk.{name}.W"),
+        "dY": bf16_normal((tokens, out_features), 1e-3, seed=seed, name=f"blk.{name}.dY"),
+    }
