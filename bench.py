@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize each tensor with separate row-wise and column-wise passes")
+    ap.add_argument("--no-bf16-sweep", action="store_true",
+                    help="skip the BF16 library GEMM comparison sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a 1 GiB device-to-device copy (the known-size reference "
                          "that scales rocprofv3 FETCH_SIZE/WRITE_SIZE counts to bytes)")
@@ -262,6 +264,10 @@ def main():
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
     components["moe_gate_up_per_expert_scaling"] = per_group_component(
         torch, mxq, X, Wgu, offs_d, w_off_gu, M)
+    if not args.no_bf16_sweep:
+        components["bf16_vs_mx_forward_sweep"] = bf16_sweep(torch, mxq)
+        components["bf16_moe_step"] = bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts,
+                                                    ms_step)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -378,6 +384,84 @@ def per_group_component(torch, mxq, X, Wgu, offs_d, w_off_gu, M, reps=5):
         "quant_W_gu": {"us": t_qw * 1e3, "GB_per_s_algorithmic": gb(Wgu.numel(), t_qw)},
         "grouped_gemm": {"us": t_g * 1e3, "TFLOP_per_s": flops / (t_g * 1e-3) / 1e12},
     }
+
+
+def bf16_sweep(torch, mxq, reps=10):
+    """Context, not part of the step: forward Linears of the block in BF16
+    through torch.matmul (the ROCm BLAS library) against the MX path (row
+    quantization of input and weight, then the MX GEMM) over token counts, as
+    a per-shape answer to "is MXFP8 at least as fast as BF16"."""
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e3
+
+    out = []
+    for name, fin, fout in (("o_proj", HIDDEN, HIDDEN), ("shared_gate", HIDDEN, 2 * FFN)):
+        w = (torch.randn(fout, fin, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        for tokens in (1024, 4096, 16384):
+            x = torch.randn(tokens, fin, device="cuda", generator=g).to(torch.bfloat16)
+            t_bf16 = timed(lambda: torch.matmul(x, w.t()))
+            xq, xs = mxq.mx_quantize_rowwise(x)
+            wq, ws = mxq.mx_quantize_rowwise(w)
+            t_gemm = timed(lambda: mxq.mx_gemm(xq, xs, wq, ws))
+            t_all = timed(lambda: mxq.mx_gemm(*mxq.mx_quantize_rowwise(x),
+                                              *mxq.mx_quantize_rowwise(w)))
+            out.append({"linear": name, "in": fin, "out": fout, "tokens": tokens,
+                        "bf16_us": t_bf16, "mx_gemm_us": t_gemm, "mx_incl_quant_us": t_all,
+                        "speedup_gemm": t_bf16 / t_gemm, "speedup_incl_quant": t_bf16 / t_all})
+    return out
+
+
+def bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts, mx_ms, reps=5):
+    """Context, not part of the step: the same six expert-layer products in
+    BF16 through torch's grouped matmul (no quantization; the transposed
+    operand copies it needs are made before timing)."""
+    if not hasattr(torch, "_grouped_mm"):
+        return {"skipped": "torch._grouped_mm not available"}
+    ends = torch.from_numpy(counts.cumsum()).to(torch.int32).cuda()
+    wgu = Wgu.view(E, 2 * FFN, HIDDEN)
+    wdn = Wdn.view(E, HIDDEN, FFN)
+    wguT = wgu.transpose(1, 2).contiguous()          # [E, 2048, 2816]
+    wdnT = wdn.transpose(1, 2).contiguous()          # [E, 1408, 2048]
+    dYT = dY.t().contiguous()                        # [2048, M]
+    dGUT = dGU.t().contiguous()                      # [2816, M]
+
+    def step():
+        torch._grouped_mm(X, wguT, offs=ends)        # gate/up forward
+        torch._grouped_mm(h, wdnT, offs=ends)        # down forward
+        torch._grouped_mm(dY, wdn, offs=ends)        # down data gradient
+        torch._grouped_mm(dGU, wgu, offs=ends)       # gate/up data gradient
+        torch._grouped_mm(dYT, h, offs=ends)         # down weight gradient [E, 2048, 1408]
+        torch._grouped_mm(dGUT, X, offs=ends)        # gate/up weight gradient [E, 2816, 2048]
+
+    try:
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            step()
+        e.record()
+        torch.cuda.synchronize()
+    except Exception as ex:                           # report, do not fail the bench
+        return {"skipped": "torch._grouped_mm failed: %s" % repr(ex)[:200]}
+    ms = s.elapsed_time(e) / reps
+    flops = 3 * 2 * int(counts.sum()) * (2 * FFN * HIDDEN + HIDDEN * FFN)
+    return {"ms_per_step": ms, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+            "mx_step_speedup": ms / mx_ms}
 
 
 def cpu_baseline(fw, bw, budget_s):
