@@ -78,3 +78,26 @@ def pg_dequantize(codes, scales, offsets):
         if hi > lo:
             out[lo:hi] = pt_dequantize(codes[lo:hi], scales[e])
     return out
+
+
+def pg_quantize_colwise(x_bf16_bits, offsets):
+    """The transposed copy of the per-group quantization, for products that
+    contract over the rows (the weight gradient over each expert's tokens, the
+    data gradient over a weight's output rows).  [HP329] §3: with per-tensor
+    or per-group FP32 scales the quantized data do not depend on the
+    direction, only the operand layout does; the transposed copy therefore
+    holds the same codes as ``pg_quantize``.  The layout follows the grouped
+    column-wise MX copy: each group padded with zero rows to a multiple of 32.
+
+    Returns (codesT uint8 [K, M_pad], scales float32 [E], padded offsets
+    int64 [E+1])."""
+    bits = np.asarray(x_bf16_bits, dtype=np.uint16)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    codes, scales = pg_quantize(bits, offsets)
+    counts = np.diff(offsets)
+    poff = np.concatenate([[0], np.cumsum((counts + 31) // 32 * 32)]).astype(np.int64)
+    out = np.zeros((bits.shape[1], int(poff[-1])), dtype=np.uint8)
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        out[:, int(poff[e]):int(poff[e]) + (hi - lo)] = codes[lo:hi].T
+    return out, scales, poff

@@ -177,3 +177,27 @@ def test_per_group_dequantize_exact():
     exp = np.array([[0.5, -1.0], [224.0, 0.0], [2.0 ** -10, -0.0],
                     [2.0 ** -4, 0.5], [-(2.0 ** -3), 2.0 ** -9]])
     assert np.array_equal(d, exp)
+
+
+def test_per_group_colwise_layout_and_codes():
+    """The transposed copy: group e's rows appear as columns starting at its
+    padded offset (multiples of 32), padding columns are +0 codes, and every
+    code equals the row-major copy's (direction does not change the data)."""
+    counts = [33, 0, 1, 64, 5]
+    offs = _groups(counts)
+    x = workloads.bf16_normal((sum(counts), 40), 1.0, seed=14, name="pgc",
+                              outlier_frac=0.02, outlier_scale=20.0)
+    cT, sT, poff = per_tensor.pg_quantize_colwise(x, offs)
+    c, s = per_tensor.pg_quantize(x, offs)
+    assert poff.tolist() == [0, 64, 64, 96, 160, 192]
+    assert cT.shape == (40, 192)
+    assert np.array_equal(sT, s)
+    for e in range(len(counts)):
+        lo, hi, p = offs[e], offs[e + 1], poff[e]
+        assert np.array_equal(cT[:, p:p + hi - lo], c[lo:hi].T)
+        assert np.all(cT[:, p + hi - lo:poff[e + 1]] == 0)
+    # dequantized transposed copy times its scales reproduces the row-major values
+    d = per_tensor.pg_dequantize(c, s, offs)
+    for e in range(len(counts)):
+        lo, hi, p = offs[e], offs[e + 1], poff[e]
+        assert np.array_equal(per_tensor.pt_dequantize(cT[:, p:p + hi - lo], s[e]), d[lo:hi].T)
