@@ -262,8 +262,8 @@ def main():
                   "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
     if not args.no_dense:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
-    components["moe_gate_up_per_expert_scaling"] = per_group_component(
-        torch, mxq, X, Wgu, offs_d, w_off_gu, M)
+    components["per_expert_scaling_step"] = per_expert_step(
+        torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
     if not args.no_bf16_sweep:
         components["bf16_vs_mx_forward_sweep"] = bf16_sweep(torch, mxq)
         components["bf16_moe_step"] = bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts,
@@ -356,34 +356,47 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
     }
 
 
-def per_group_component(torch, mxq, X, Wgu, offs_d, w_off_gu, M, reps=5):
-    """Second format on the MoE gate/up forward: per-expert current scaling
-    (one FP32 scale per expert group of X rows and per expert weight) and the
-    grouped GEMM with per-group scales."""
-    def timed(fn, *a):
-        for _ in range(2):
-            r = fn(*a)
-        torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            r = fn(*a)
-        e.record()
-        torch.cuda.synchronize()
-        return r, s.elapsed_time(e) / reps
+def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops,
+                    steps=5):
+    """The second format on the same expert-layer step: per-expert current
+    scaling (one FP32 scale per expert group of rows and per expert weight),
+    every tensor quantized row-major and transposed each step, the six
+    products on the per-group-scaled grouped GEMMs."""
+    def step():
+        xq, xs = mxq.fp8_quantize_per_group(X, offs_d)
+        wq, ws = mxq.fp8_quantize_per_group(Wgu, w_off_gu)
+        mxq.fp8_grouped_gemm_per_group(xq, xs, wq.view(E, 2 * FFN, HIDDEN), ws, offs_d)
+        hq, hs = mxq.fp8_quantize_per_group(h, offs_d)
+        dq, dsc = mxq.fp8_quantize_per_group(Wdn, w_off_dn)
+        mxq.fp8_grouped_gemm_per_group(hq, hs, dq.view(E, HIDDEN, FFN), dsc, offs_d)
+        gq, gs = mxq.fp8_quantize_per_group(dY, offs_d)
+        dnT, dnTs, _ = mxq.fp8_quantize_per_group_colwise(Wdn, w_off_dn)      # [1408, E*2048]
+        mxq.fp8_grouped_gemm_per_group(
+            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dnTs, offs_d)
+        uq, us = mxq.fp8_quantize_per_group(dGU, offs_d)
+        guT, guTs, _ = mxq.fp8_quantize_per_group_colwise(Wgu, w_off_gu)      # [2048, E*2816]
+        mxq.fp8_grouped_gemm_per_group(
+            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), guTs, offs_d)
+        dyT, dyTs, poff = mxq.fp8_quantize_per_group_colwise(dY, offs_d)
+        hT, hTs, _ = mxq.fp8_quantize_per_group_colwise(h, offs_d)
+        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, dyTs, hT, hTs, poff)
+        duT, duTs, _ = mxq.fp8_quantize_per_group_colwise(dGU, offs_d)
+        xT, xTs, _ = mxq.fp8_quantize_per_group_colwise(X, offs_d)
+        mxq.fp8_grouped_gemm_wgrad_per_group(duT, duTs, xT, xTs, poff)
 
-    (xq, xs), t_qx = timed(mxq.fp8_quantize_per_group, X, offs_d)
-    (wq, ws), t_qw = timed(mxq.fp8_quantize_per_group, Wgu, w_off_gu)
-    _, t_g = timed(mxq.fp8_grouped_gemm_per_group, xq, xs, wq.view(E, 2 * FFN, HIDDEN), ws,
-                   offs_d)
-    flops = 2 * M * 2 * FFN * HIDDEN
-    gb = lambda n, ms: n * 3 / (ms * 1e-3) / 1e9
-    return {
-        "quant_X": {"us": t_qx * 1e3, "GB_per_s_algorithmic": gb(X.numel(), t_qx)},
-        "quant_W_gu": {"us": t_qw * 1e3, "GB_per_s_algorithmic": gb(Wgu.numel(), t_qw)},
-        "grouped_gemm": {"us": t_g * 1e3, "TFLOP_per_s": flops / (t_g * 1e-3) / 1e12},
-    }
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
+            "quantization": "per-expert FP32 scales, row-major and transposed copies"}
 
 
 def bf16_sweep(torch, mxq, reps=10):

@@ -394,8 +394,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     if (hi_t > (g.K & ~31LL)) hi_t = g.K & ~31LL;     // g.K holds the token capacity
     kdim = hi_t > lo_t ? hi_t - lo_t : 0;
     c_rows = g.M - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, lo_t, c_rows, kdim, true, SW);
-    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, lo_t, g.N - n0, kdim, true, SW);
+    group = e;
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, lo_t, c_rows, kdim, !PT, SW);
+    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, lo_t, g.N - n0, kdim, !PT, SW);
     cbase = static_cast<uint8_t*>(g.c) + (int64_t)e * g.M * g.ldc * (OUT == MXQ_OUT_FP32 ? 4 : 2);
   }
 
@@ -836,6 +837,30 @@ extern "C" int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scale
   g.offsets = offsets; g.E = E;
   const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
   return launch_gemm<kVarM, true>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
+}
+
+extern "C" int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* a_scales,
+                                                int64_t lda_t, const uint8_t* bt,
+                                                const float* b_scales, int64_t ldb_t,
+                                                const int64_t* offsets_padded, int32_t E,
+                                                int64_t N, int64_t K, void* c, int64_t ldc,
+                                                int out_dtype, int accum, hipStream_t stream) {
+  int st = check_common(N, K, 0, ldc, out_dtype, accum);
+  if (st) return st;
+  if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets_padded || !a_scales || !b_scales) return MXQ_ERR_NULL;
+  if (N == 0 || K == 0) return MXQ_OK;
+  if (!c || !at || !bt) return MXQ_ERR_NULL;
+  if (lda_t % 16 != 0 || ldb_t % 16 != 0 || !aligned(at, 16) || !aligned(bt, 16))
+    return MXQ_ERR_ALIGN;
+  const int64_t cap = lda_t < ldb_t ? lda_t : ldb_t;    // token capacity of both operands
+  if (!fits32(lda_t, cap) || !fits32(ldb_t, cap)) return MXQ_ERR_SHAPE;
+  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
+  GemmArgs g = make_args(at, nullptr, lda_t, 0, bt, nullptr, ldb_t, 0, N, K, cap, c, ldc);
+  g.pta = a_scales; g.ptb = b_scales;
+  g.offsets = offsets_padded; g.E = E;
+  const int64_t blocks = (int64_t)E * ((N + TM - 1) / TM) * g.tiles_n;
+  return launch_gemm<kVarK, true>(g, blocks, out_dtype, stream);
 }
 
 extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t,

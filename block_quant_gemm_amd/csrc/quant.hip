@@ -98,6 +98,18 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
   }
 }
 
+// Correctly rounded FP32 quotient x / s (s > 0) for the current-scaling
+// encoders: q0 = RN(x * r) with r = RN(1/s) and one FMA correction
+// RN(q0 + RN'(x - s*q0) * r) (Markstein); a subnormal s divides directly.
+__device__ __forceinline__ float pt_div(float xv, float s, float r, bool direct) {
+  if (direct) return __fdiv_rn(xv, s);
+  float q0 = xv * r;
+  float rem = __builtin_fmaf(-q0, s, xv);
+  // s > 0, so the quotient has the sign of x; the correction step alone
+  // would turn -0 into +0.
+  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), xv);
+}
+
 // ---------------------------------------------------------------------------
 // Column-wise (grouped, zero-padded) MX quantization, transposed output.
 //
@@ -129,13 +141,17 @@ constexpr int kColDualGroup = 4;  // column tiles per dispatch block (dual-axis)
 // codes and scales of every source row it holds.  Lane tid has 8 consecutive
 // columns of a row, and the 4 lanes of a DPP quad one 32-block of it (K is a
 // multiple of 32), so the row quantizer's block step applies unchanged.
-template <bool ROW>
+// PG (per-group current scaling, transposed copy): no block scales; every
+// 32-row block takes its group's FP32 scale (gscale, with gmax the group's
+// |x| maximum pattern) and encodes as the per-tensor pass does.
+template <bool ROW, bool PG = false>
 __global__ __launch_bounds__(256) void k_mx_colwise(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const int64_t* __restrict__ offsets, int32_t E,
     uint8_t* __restrict__ qT, int64_t ldqT, int64_t M_cap,
     uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ sc, int64_t lds) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ sc, int64_t lds,
+    const uint32_t* __restrict__ gmax = nullptr, const float* __restrict__ gscale = nullptr) {
   __shared__ uint32_t tile[kColTileM * kColLdsW];
   __shared__ __attribute__((aligned(16))) uint8_t outq[kColTileK * kColOutW];
   __shared__ __attribute__((aligned(16))) uint8_t outs[kColTileK * 4];
@@ -143,6 +159,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   __shared__ int64_t s_poff[kColMaxGroupsLds + 1];
   __shared__ int64_t s_src0[4];
   __shared__ int32_t s_nvalid[4];
+  __shared__ int32_t s_grp[4];
 
   const int tid = threadIdx.x;
   // Workgroups along K are consecutive in dispatch order, so the ones in
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     // poff[g] <= col < poff[g+1] (binary search over the non-decreasing poff).
     int64_t col = p0 + 32 * tid;
     int64_t src0 = 0;
-    int32_t nvalid = 0;
+    int32_t nvalid = 0, grp = -1;
     if (col < s_poff[G] && col < M_cap) {
       int lo = 0, hi = G - 1;
       while (lo < hi) {
@@ -212,9 +229,11 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
       src0 = r0;
       int64_t n = r1 - r0;
       nvalid = n <= 0 ? 0 : (n >= 32 ? 32 : (int32_t)n);
+      grp = lo;
     }
     s_src0[tid] = src0;
     s_nvalid[tid] = nvalid;
+    s_grp[tid] = grp;
   }
   __syncthreads();
 
@@ -273,32 +292,63 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     uint32_t vals[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) vals[j] = tile[(rbase + j) * kColLdsW + p];
-    u16x2 m = __builtin_bit_cast(u16x2, 0u);
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) m = __builtin_elementwise_max(m, absmax2(vals[j], vals[j + 1]));
-    uint32_t mw = __builtin_bit_cast(uint32_t, m);
-    uint32_t ow = dpp_u32(mw, kQuadXor1);           // partner lane^1: other half
-    u16x2 mm = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ow));
-    uint32_t code0 = mx_scale_code(mm.x);           // column 2p
-    uint32_t code1 = mx_scale_code(mm.y);           // column 2p+1
-    float inv0 = mx_inv_scale(code0 == 0xFFu ? 127u : code0);
-    float inv1 = mx_inv_scale(code1 == 0xFFu ? 127u : code1);
     uint32_t c0[4], c1[4];
+    uint32_t code0 = 0, code1 = 0;
+    if (PG) {
+      // Padding rows were loaded as zeros and encode to +0.  A group whose
+      // amax is NaN/Inf has s = 1: Inf saturates, NaN becomes 0x7F | sign.
+      const int e = s_grp[w];
+      const float gs = e >= 0 ? gscale[e] : 1.0f;
+      const bool nonfinite = e >= 0 && gmax[e] >= 0x7F80u;
+      const bool direct = gs < 1.17549435e-38f;    // subnormal scale: divide directly
+      const float rc = __frcp_rn(gs);
+      // x / 1 is x; dividing would turn +-Inf into NaN through the correction step
+      auto enc = [&](float v) { return nonfinite ? v : pt_div(v, gs, rc, direct); };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
-      uint32_t t0 = cvt2_e4m3_sat<false>(bf16_lo(a) * inv0, bf16_lo(b2) * inv0, 0u);
-      c0[j] = cvt2_e4m3_sat<true>(bf16_lo(c) * inv0, bf16_lo(d) * inv0, t0);
-      uint32_t t1 = cvt2_e4m3_sat<false>(bf16_hi(a) * inv1, bf16_hi(b2) * inv1, 0u);
-      c1[j] = cvt2_e4m3_sat<true>(bf16_hi(c) * inv1, bf16_hi(d) * inv1, t1);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
+        uint32_t t0 = cvt2_e4m3_sat<false>(enc(bf16_lo(a)), enc(bf16_lo(b2)), 0u);
+        c0[j] = cvt2_e4m3_sat<true>(enc(bf16_lo(c)), enc(bf16_lo(d)), t0);
+        uint32_t t1 = cvt2_e4m3_sat<false>(enc(bf16_hi(a)), enc(bf16_hi(b2)), 0u);
+        c1[j] = cvt2_e4m3_sat<true>(enc(bf16_hi(c)), enc(bf16_hi(d)), t1);
+        if (nonfinite) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t v = vals[4 * j + r];
+            if ((v & 0x7FFFu) > 0x7F80u)
+              c0[j] = (c0[j] & ~(0xFFu << (8 * r))) | ((0x7Fu | ((v >> 8) & 0x80u)) << (8 * r));
+            if (((v >> 16) & 0x7FFFu) > 0x7F80u)
+              c1[j] = (c1[j] & ~(0xFFu << (8 * r))) | ((0x7Fu | ((v >> 24) & 0x80u)) << (8 * r));
+          }
+        }
+      }
+    } else {
+      u16x2 m = __builtin_bit_cast(u16x2, 0u);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) m = __builtin_elementwise_max(m, absmax2(vals[j], vals[j + 1]));
+      uint32_t mw = __builtin_bit_cast(uint32_t, m);
+      uint32_t ow = dpp_u32(mw, kQuadXor1);         // partner lane^1: other half
+      u16x2 mm = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ow));
+      code0 = mx_scale_code(mm.x);                  // column 2p
+      code1 = mx_scale_code(mm.y);                  // column 2p+1
+      float inv0 = mx_inv_scale(code0 == 0xFFu ? 127u : code0);
+      float inv1 = mx_inv_scale(code1 == 0xFFu ? 127u : code1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t a = vals[4 * j], b2 = vals[4 * j + 1], c = vals[4 * j + 2], d = vals[4 * j + 3];
+        uint32_t t0 = cvt2_e4m3_sat<false>(bf16_lo(a) * inv0, bf16_lo(b2) * inv0, 0u);
+        c0[j] = cvt2_e4m3_sat<true>(bf16_lo(c) * inv0, bf16_lo(d) * inv0, t0);
+        uint32_t t1 = cvt2_e4m3_sat<false>(bf16_hi(a) * inv1, bf16_hi(b2) * inv1, 0u);
+        c1[j] = cvt2_e4m3_sat<true>(bf16_hi(c) * inv1, bf16_hi(d) * inv1, t1);
+      }
+      if (code0 == 0xFFu) c0[0] = c0[1] = c0[2] = c0[3] = 0x7F7F7F7Fu;
+      if (code1 == 0xFFu) c1[0] = c1[1] = c1[2] = c1[3] = 0x7F7F7F7Fu;
     }
-    if (code0 == 0xFFu) c0[0] = c0[1] = c0[2] = c0[3] = 0x7F7F7F7Fu;
-    if (code1 == 0xFFu) c1[0] = c1[1] = c1[2] = c1[3] = 0x7F7F7F7Fu;
     *reinterpret_cast<uint4*>(&outq[(2 * p) * kColOutW + w * 32 + h * 16]) =
         make_uint4(c0[0], c0[1], c0[2], c0[3]);
     *reinterpret_cast<uint4*>(&outq[(2 * p + 1) * kColOutW + w * 32 + h * 16]) =
         make_uint4(c1[0], c1[1], c1[2], c1[3]);
-    if (h == 0) {
+    if (!PG && h == 0) {
       outs[(2 * p) * 4 + w] = (uint8_t)code0;
       outs[(2 * p + 1) * 4 + w] = (uint8_t)code1;
     }
@@ -313,7 +363,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
         store_stream(qT + k * ldqT + col,
                      *reinterpret_cast<const uint4*>(&outq[row * kColOutW + c16 * 16]));
     }
-    if (tid < kColTileK && kb + tid < K) {
+    if (!PG && tid < kColTileK && kb + tid < K) {
       uint8_t* d = scT + (kb + tid) * ldsT + (p0 >> 5);
       const uint32_t sv = *reinterpret_cast<const uint32_t*>(&outs[tid * 4]);
       if (scale_dword) {
@@ -378,15 +428,6 @@ __global__ __launch_bounds__(kPtThreads) void k_pt_amax(const uint16_t* __restri
   }
   m = block_max_u32(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
-}
-
-__device__ __forceinline__ float pt_div(float xv, float s, float r, bool direct) {
-  if (direct) return __fdiv_rn(xv, s);
-  float q0 = xv * r;
-  float rem = __builtin_fmaf(-q0, s, xv);
-  // s > 0, so the quotient has the sign of x; the correction step alone
-  // would turn -0 into +0.
-  return __builtin_copysignf(__builtin_fmaf(rem, r, q0), xv);
 }
 
 // Codes of two BF16 values packed in w, for a tensor whose amax is NaN/Inf
@@ -706,6 +747,53 @@ extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, i
   if (st != MXQ_OK || M == 0 || K == 0) return st;
   hipLaunchKernelGGL(k_pg_quant, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
                      offsets, E, gmax, scales, q, ldq);
+  return launch_status();
+}
+
+extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K,
+                                              int64_t ldx, const int64_t* offsets, int32_t E,
+                                              uint8_t* qT, int64_t ldqT, int64_t M_cap,
+                                              float* scales, int64_t* offsets_padded,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
+  if (K % 8 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  if (K > 0 && M_cap > 0) {
+    if (!qT || (M > 0 && !x)) return MXQ_ERR_NULL;
+    if (ldqT < M_cap || (M > 0 && ldx < K)) return MXQ_ERR_SHAPE;
+    if (ldqT % 16 != 0 || !aligned(qT, 16) || (M > 0 && (ldx % 8 != 0 || !aligned(x, 16))))
+      return MXQ_ERR_ALIGN;
+  }
+  if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
+    return MXQ_ERR_WORKSPACE;
+  uint32_t* rowmax = static_cast<uint32_t*>(workspace);
+  uint32_t* gmax = rowmax + M;
+  const int64_t waves = (int64_t)num_cus() * 64;
+  const int64_t rows_blocks = (M + 3) / 4;
+  const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
+                                                             : waves / 4);
+  if (M > 0 && K > 0) {
+    hipLaunchKernelGGL(k_pg_rowmax, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
+                       rowmax);
+  } else if (M > 0) {
+    hipLaunchKernelGGL(k_fill_u32, dim3((uint32_t)((M + 255) / 256)), dim3(256), 0, stream,
+                       rowmax, M, 0u);
+  }
+  int st = launch_status();
+  if (st != MXQ_OK) return st;
+  hipLaunchKernelGGL(k_pg_scale, dim3((uint32_t)E), dim3(kPgThreads), 0, stream, rowmax, offsets,
+                     M, gmax, scales);
+  st = launch_status();
+  if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
+  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
+  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  hipLaunchKernelGGL((k_mx_colwise<false, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
+                     x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded,
+                     nullptr, 0, nullptr, 0, gmax, scales);
   return launch_status();
 }
 

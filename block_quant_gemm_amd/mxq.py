@@ -39,6 +39,11 @@ _SIGS = {
     "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _i32,
                                        _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                        ctypes.c_int, _p]),
+    "fp8_quantize_per_group_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64,
+                                                      _i64, _p, _p, _p, _sz, _p]),
+    "fp8_grouped_gemm_wgrad_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _p, _i32,
+                                                        _i64, _i64, _p, _i64, ctypes.c_int,
+                                                        ctypes.c_int, _p]),
     "fp8_grouped_gemm_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p, _i32,
                                                   _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                                   ctypes.c_int, _p]),
@@ -224,6 +229,32 @@ def fp8_quantize_per_group(x, offsets, q=None, scales=None, workspace=None):
     return q, scales
 
 
+def fp8_quantize_per_group_colwise(x, offsets, M_cap=None, qT=None, scales=None,
+                                   offsets_padded=None, workspace=None):
+    """Transposed copy of fp8_quantize_per_group: returns (codesT uint8
+    [K, M_cap] with each group padded to 32 columns, scales float32 [E],
+    offsets_padded int64 [E+1])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = offsets.numel() - 1
+    if M_cap is None:
+        M_cap = colwise_capacity(M, E)
+    if qT is None:
+        qT = torch.empty((K, M_cap), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(E, dtype=torch.float32, device=x.device)
+    if offsets_padded is None:
+        offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
+    ws = workspace_size(WS_PER_GROUP, M, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 4), dtype=torch.uint8, device=x.device)
+    _check(load().fp8_quantize_per_group_colwise(_ptr(x), M, K, x.stride(0), _ptr(offsets), E,
+                                                 _ptr(qT), qT.stride(0), M_cap, _ptr(scales),
+                                                 _ptr(offsets_padded), _ptr(workspace),
+                                                 workspace.numel(), _stream()))
+    return qT, scales, offsets_padded
+
+
 # ---------------------------------------------------------------------------
 # GEMMs
 # ---------------------------------------------------------------------------
@@ -301,6 +332,23 @@ def expert_view(qT, sT, E, rows_per_expert):
     q = qT.as_strided((E, K, R), (R, qT.stride(0), 1))
     s = sT.as_strided((E, K, R // 32), (R // 32, sT.stride(0), 1))
     return q, s
+
+
+def fp8_grouped_gemm_wgrad_per_group(at, a_scales, bt, b_scales, offsets_padded,
+                                     out_dtype=OUT_BF16, accum=ACC_MFMA_FP8, c=None):
+    """Per-group-scaled weight gradient: dW[e] = s_a[e] s_b[e] Aᵀ[:, group e] ·
+    (Bᵀ[:, group e])ᵀ on fp8_quantize_per_group_colwise copies.  Returns dW [E, N, K]."""
+    N = at.shape[0]
+    K = bt.shape[0]
+    E = offsets_padded.numel() - 1
+    if c is None:
+        dt = torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32
+        c = torch.empty((E, N, K), dtype=dt, device=at.device)
+    _check(load().fp8_grouped_gemm_wgrad_per_group(_ptr(at), _ptr(a_scales), at.stride(0),
+                                                   _ptr(bt), _ptr(b_scales), bt.stride(0),
+                                                   _ptr(offsets_padded), E, N, K, _ptr(c),
+                                                   c.stride(1), out_dtype, accum, _stream()))
+    return c
 
 
 def mx_grouped_gemm_wgrad(at, at_scale, bt, bt_scale, offsets_padded, out_dtype=OUT_BF16,

@@ -181,6 +181,28 @@ MXQ_API int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int6
                            uint8_t* q, int64_t ldq, float* scales,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Transposed copy of the per-group current-scaling quantization, for the
+ * products that contract over x's rows: the weight gradient over each
+ * expert's tokens, the data gradient over a weight's output rows.  [HP329]
+ * §3: with FP32 per-tensor / per-group scales the quantized data do not
+ * depend on the GEMM direction, only the operand layout does, so the codes
+ * and scales equal fp8_quantize_per_group's; the layout is that of
+ * mx_quantize_colwise: group e's rows become columns
+ * [offsets_padded[e], offsets_padded[e] + count_e) of qT, each group padded
+ * with zero columns to a multiple of 32, columns past the padded total
+ * zero-filled.
+ *   x, offsets, E, scales, workspace : as fp8_quantize_per_group.
+ *   qT            : device, E4M3 [K, M_cap], row stride ldqT bytes (% 16 == 0),
+ *                   16-byte aligned; M_cap % 32 == 0 (M + 31*E is always enough).
+ *   offsets_padded: device int64 [E+1] receiving the padded offsets, or NULL.
+ */
+MXQ_API int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   const int64_t* offsets, int32_t E,
+                                   uint8_t* qT, int64_t ldqT, int64_t M_cap, float* scales,
+                                   int64_t* offsets_padded, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * GEMMs                                                                     *
  * ------------------------------------------------------------------------ */
@@ -290,6 +312,21 @@ MXQ_API int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scales, 
                                int64_t M, int64_t N, int64_t K,
                                void* c, int64_t ldc, int out_dtype, int accum,
                                hipStream_t stream);
+
+/*
+ * Weight gradient with per-group FP32 scales (variable K, the per-expert
+ * current-scaling counterpart of mx_grouped_gemm_wgrad): for each group e,
+ *   dW_e[N, K] = a_scales[e] * b_scales[e] * Σ_{t in [poff[e], poff[e+1])} at[:, t] · bt[:, t]ᵀ
+ * with at [N, ld], bt [K, ld] from fp8_quantize_per_group_colwise (same
+ * offsets) and a_scales, b_scales device float[E].  Output, strides and
+ * requirements as mx_grouped_gemm_wgrad without the block scales.
+ */
+MXQ_API int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* a_scales, int64_t lda_t,
+                                     const uint8_t* bt, const float* b_scales, int64_t ldb_t,
+                                     const int64_t* offsets_padded, int32_t E,
+                                     int64_t N, int64_t K,
+                                     void* c, int64_t ldc, int out_dtype, int accum,
+                                     hipStream_t stream);
 
 MXQ_API int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t, int64_t ldsa_t,
                           const uint8_t* bt, const uint8_t* bt_scale, int64_t ldb_t, int64_t ldsb_t,

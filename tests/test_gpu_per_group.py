@@ -190,3 +190,158 @@ def test_per_group_gate_up_full_size_sampled():
         sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y)
     ch = host(c)[rows, n]
     assert gemm.check_bf16_extra(ch, Y, S, T).all()
+
+
+# ---------------------------------------------------------------------------
+# transposed copy (dgrad / wgrad operands)
+# ---------------------------------------------------------------------------
+
+def _colwise(bits, offs, M_cap=None):
+    qT, s, poff = mxq.fp8_quantize_per_group_colwise(to_dev_bf16(bits), to_dev(offs),
+                                                     M_cap=M_cap)
+    return qT, s, poff, host(qT), host(s), host(poff)
+
+
+def _assert_colwise_equal(bits, offs, qTh, sh, ph):
+    rq, rs, rp = per_tensor.pg_quantize_colwise(bits, offs)
+    assert np.array_equal(ph, rp)
+    assert np.array_equal(sh.view(np.uint32), rs.view(np.uint32))
+    Mp = int(rp[-1])
+    if not np.array_equal(qTh[:, :Mp], rq):
+        bad = np.argwhere(qTh[:, :Mp] != rq)[:8]
+        raise AssertionError(f"codes differ at {bad.tolist()}")
+    assert np.all(qTh[:, Mp:] == 0), "columns past the padded total"
+
+
+@pytest.mark.parametrize("counts,K", [
+    ([40, 0, 1, 130, 0, 300, 0], 64),
+    ([0, 0, 257], 136),
+    ([5], 8),
+    ([1000, 17, 0, 2, 511], 2048),
+])
+def test_per_group_colwise_bit_exact(counts, K):
+    say(f"per-group colwise counts={counts} K={K}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    x = workloads.bf16_normal((int(counts.sum()), K), 1.0, seed=K + 1, name="pgcx",
+                              outlier_frac=0.01, outlier_scale=100.0)
+    _, _, _, qTh, sh, ph = _colwise(x, offs)
+    _assert_colwise_equal(x, offs, qTh, sh, ph)
+
+
+def test_per_group_colwise_special_groups_and_capacity():
+    """NaN / Inf / zero / subnormal-scale groups, and a capacity well past the
+    padded total (zero-filled)."""
+    say("per-group colwise special groups")
+    counts = np.array([8, 40, 8, 0, 33, 8], np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    K = 96
+    x = workloads.bf16_normal((int(counts.sum()), K), 1.0, seed=6, name="pgcs")
+    x[offs[0] + 2, 7] = 0xFFC0                        # -NaN in group 0
+    x[offs[1] + 5, 1] = 0x7F80                        # +Inf in group 1
+    x[offs[1] + 9, 3] = 0xFFC0                        # and a NaN
+    x[offs[2]:offs[3]] = 0x8000                       # -0 in group 2
+    tiny = workloads.bf16_normal((33, K), 1.0, seed=7, name="pgct")
+    v = codec.bf16_bits_to_f64(tiny) * 2.0 ** -122
+    x[offs[4]:offs[5]] = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+    _, _, _, qTh, sh, ph = _colwise(x, offs, M_cap=512)
+    _assert_colwise_equal(x, offs, qTh, sh, ph)
+
+
+def test_per_group_colwise_full_size_sampled_columns():
+    """dGU [49152, 2816] over the 64 Zipf groups: 32 sampled columns."""
+    say("per-group colwise dGU 49152x2816")
+    counts = workloads.moe_counts(0)
+    offs = workloads.offsets_from_counts(counts)
+    dGU = workloads.moe_backward(0)["dGU"]
+    qT, s, poff, _, sh, ph = _colwise(dGU, offs)
+    # the group scales depend on every column: take them from the full tensor
+    rq, rs = per_tensor.pg_quantize(dGU, offs)
+    assert np.array_equal(sh.view(np.uint32), rs.view(np.uint32))
+    cols = np.random.default_rng(3).choice(dGU.shape[1], 32, replace=False)
+    rp = np.concatenate([[0], np.cumsum((np.diff(offs) + 31) // 32 * 32)])
+    assert np.array_equal(ph, rp)
+    qh = host(qT[torch.from_numpy(cols).cuda()])
+    for e in range(len(offs) - 1):
+        lo, hi, p = int(offs[e]), int(offs[e + 1]), int(rp[e])
+        assert np.array_equal(qh[:, p:p + hi - lo], rq[lo:hi, cols].T)
+        assert np.all(qh[:, p + hi - lo:int(rp[e + 1])] == 0)
+
+
+def _dequant_colwise(qTh, sh, ph):
+    """Exact values of a transposed per-group copy: group columns times their scale."""
+    out = np.zeros(qTh.shape)
+    for e in range(len(ph) - 1):
+        lo, hi = int(ph[e]), int(ph[e + 1])
+        if hi > lo:
+            out[:, lo:hi] = per_tensor.pt_dequantize(qTh[:, lo:hi], sh[e])
+    return out
+
+
+@pytest.mark.parametrize("counts,N,K", [
+    ([40, 0, 1, 130, 0, 300, 0], 160, 96),
+    ([300, 0, 45, 513], 296, 768),
+])
+@pytest.mark.parametrize("out", [mxq.OUT_BF16, mxq.OUT_FP32])
+def test_per_group_wgrad(counts, N, K, out):
+    say(f"per-group wgrad counts={counts} N={N} K={K} out={out}")
+    counts = np.array(counts, np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    E, T = len(counts), int(counts.sum())
+    dy = workloads.bf16_normal((T, N), 1e-3, seed=T + N, name="pgwd", outlier_frac=0.005,
+                               outlier_scale=30.0)
+    x = workloads.bf16_normal((T, K), 1.0, seed=T + K, name="pgwx")
+    aT, sa, poff, aTh, sah, ph = _colwise(dy, offs)
+    bT, sb, _, bTh, sbh, _ = _colwise(x, offs)
+    c = mxq.fp8_grouped_gemm_wgrad_per_group(aT, sa, bT, sb, poff, out_dtype=out)
+    A, B = _dequant_colwise(aTh, sah, ph), _dequant_colwise(bTh, sbh, ph)
+    Y, S = gemm.grouped_wgrad_ref(A[:, :int(ph[-1])], B[:, :int(ph[-1])], ph)
+    Tb = np.zeros_like(Y)
+    for e in range(E):
+        lo, hi = int(ph[e]), int(ph[e + 1])
+        if hi > lo:
+            ones_a = np.full((N, (hi - lo) // 32), 127, np.uint8)
+            ones_b = np.full((K, (hi - lo) // 32), 127, np.uint8)
+            Tb[e] = gemm.fp8_mfma_truncation_bound(aTh[:, lo:hi], ones_a, bTh[:, lo:hi],
+                                                   ones_b) * float(sah[e]) * float(sbh[e])
+    Tb = Tb + 2.0 ** -23 * np.abs(Y)
+    if out == mxq.OUT_FP32:
+        ok = gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, Tb)
+    else:
+        ok = gemm.check_bf16_extra(host(c), Y, S, Tb)
+    say(f"  elements {ok.size}: within tolerance {ok.mean():.6f}")
+    assert ok.all()
+    for e in np.nonzero(counts == 0)[0]:
+        assert torch.all(c[e] == 0)
+
+
+def test_per_group_dgrad_with_transposed_weights():
+    """Data gradient dX = dY · W_e per expert: the weights' transposed
+    per-expert copy read in place through per-expert strides."""
+    say("per-group dgrad")
+    counts = np.array([40, 0, 130, 77], np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    E, M, N, K = 4, int(counts.sum()), 192, 320     # W_e [N, K]; dY [M, N]; dX [M, K]
+    w = workloads.bf16_normal((E * N, K), 0.02, seed=21, name="pgdw")
+    dy = workloads.bf16_normal((M, N), 1e-3, seed=21, name="pgdy")
+    woffs = np.arange(E + 1, dtype=np.int64) * N
+    wT, sw, _, wTh, swh, wph = _colwise(w, woffs)    # [K, E*N]
+    gq, sg, gh, sgh = _quant(dy, offs)
+    bview = wT[:, :E * N].view(K, E, N).permute(1, 0, 2)  # [E, K, N], expert stride N
+    c = mxq.fp8_grouped_gemm_per_group(gq, sg, bview, sw, to_dev(offs), out_dtype=mxq.OUT_FP32)
+    A = per_tensor.pg_dequantize(gh, sgh, offs)
+    Bt = _dequant_colwise(wTh, swh, wph)             # [K, E*N]
+    B = np.stack([Bt[:, e * N:(e + 1) * N] for e in range(E)])   # [E, K, N]
+    Y, S = gemm.grouped_gemm_ref(A, B, offs)
+    T = np.zeros_like(Y)
+    onesa = np.full((M, N // 32), 127, np.uint8)
+    onesb = np.full((K, N // 32), 127, np.uint8)
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            T[lo:hi] = gemm.fp8_mfma_truncation_bound(gh[lo:hi], onesa[lo:hi],
+                                                      wTh[:, e * N:(e + 1) * N], onesb) * \
+                float(sgh[e]) * float(swh[e])
+    T = T + 2.0 ** -23 * np.abs(Y)
+    assert gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T).all()

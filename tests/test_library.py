@@ -89,3 +89,25 @@ def test_per_group_validation_errors(lib):
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 250, P, 4, 8, 8, 32, P, 8, 0, 0, None) == 3
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 40, P, 8, 0, 0, None) == 2
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 32, P, 8, 0, 1, None) == 4
+
+
+def test_per_group_transposed_and_wgrad_validation_errors(lib):
+    P = 4096
+    ws = lib.mxq_workspace_size(1, 64, 4, 0, 0)
+    # fp8_quantize_per_group_colwise(x, M, K, ldx, offsets, E, qT, ldqT, M_cap, scales,
+    #                                offsets_padded, ws, ws_bytes, stream)
+    assert lib.fp8_quantize_per_group_colwise(P, -1, 32, 32, P, 4, P, 256, 256, P, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 0, P, 256, 256, P, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 36, 40, P, 4, P, 256, 256, P, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 256, 250, P, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 200, 256, P, P, P, ws, None) == 2
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 264, 256, P, P, P, ws, None) == 3
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, None, 4, P, 256, 256, P, P, P, ws, None) == 1
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 256, 256, P, P, P, ws - 4, None) == 5
+    # fp8_grouped_gemm_wgrad_per_group(at, sa, lda_t, bt, sb, ldb_t, poff, E, N, K, c, ldc,
+    #                                  out, accum, stream)
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 40, P, P, 32, P, 2, 8, 8, P, 8, 0, 0, None) == 3
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, None, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 0, None) == 1
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 0, 8, 8, P, 8, 0, 0, None) == 2
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 4, 0, 0, None) == 2
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 1, None) == 4
