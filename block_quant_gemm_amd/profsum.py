@@ -87,11 +87,16 @@ def _per_kernel(rows):
     return acc
 
 
+CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"     # the runtime's device-to-device copy
+
+
 def _copy_kib(rows):
-    """KiB the calibration copy reports: the largest copy-kernel dispatch."""
-    vals = [v for _, name, v in rows if "copy" in name.lower() and not is_lib(name)]
+    """KiB the calibration copy reports: the largest dispatch of the runtime's
+    copy kernel (the 1 GiB copy of `bench.py --copy-calibration`)."""
+    vals = [v for _, name, v in rows if name.strip('"') == CALIBRATION_KERNEL]
     if not vals:
-        raise SystemExit("no copy-kernel dispatch found (run bench.py --copy-calibration)")
+        raise SystemExit("no %s dispatch found (run bench.py --copy-calibration)"
+                         % CALIBRATION_KERNEL)
     return max(vals)
 
 
