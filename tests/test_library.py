@@ -111,3 +111,23 @@ def test_per_group_transposed_and_wgrad_validation_errors(lib):
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 0, 8, 8, P, 8, 0, 0, None) == 2
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 4, 0, 0, None) == 2
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 1, None) == 4
+
+
+def test_size_limits_rejected(lib):
+    """Sizes past what the kernels index with 32-bit offsets are rejected on
+    the host (no launch): a 256-row GEMM tile must span < 2^31 bytes, the
+    row quantizer's segment count must fit 31 bits."""
+    P = 4096
+    big_ld = (1 << 31) // 256                         # 256-row tile + K exceeds 2^31
+    assert lib.mx_gemm(P, P, big_ld, 64, P, P, 32, 1, 4, 4, 32, P, 4, 0, 0, None) == 2
+    assert lib.mx_gemm(P, P, 32, 1, P, P, big_ld, 64, 4, 4, 32, P, 4, 0, 0, None) == 2
+    assert lib.mx_grouped_gemm(P, P, big_ld, 64, P, P, 32, 1, 256, 8, P, 4, 8, 8, 32, P, 8,
+                               0, 0, None) == 2
+    assert lib.mx_grouped_gemm_wgrad(P, P, big_ld, big_ld // 32, P, P, big_ld, big_ld // 32,
+                                     P, 2, 8, 8, P, 8, 0, 0, None) == 2
+    # strided (non-contiguous) rows: 2^31 segments of 512 elements
+    rows = 1 << 29
+    assert lib.mx_quantize_rowwise(P, rows, 2048, 2056, P, 2048, P, 64, None) == 2
+    # the largest accepted tile stride passes the size check (then fails on alignment)
+    ok_ld = ((1 << 31) - 64) // 257 // 16 * 16
+    assert lib.mx_gemm(P + 2, P, ok_ld, 64, P, P, 32, 1, 4, 4, 32, P, 4, 0, 0, None) == 3
