@@ -4,6 +4,11 @@
       Markdown table of a `rocprofv3 --kernel-trace --stats` summary
       (library kernels first; durations in microseconds).
 
+  python -m block_quant_gemm_amd.profsum mfma DIR
+      Matrix-unit utilisation of each library kernel from one `rocprofv3 --pmc
+      SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE ...` run:
+      busy cycles / (active cycles per XCC x SIMDs), from the run's agent info.
+
   python -m block_quant_gemm_amd.profsum traffic --fetch DIR --write DIR -o JSON
       HBM bytes per dispatch of each library kernel from two `rocprofv3 --pmc`
       runs of `bench.py --copy-calibration` (one with FETCH_SIZE, one with
@@ -120,11 +125,43 @@ def traffic(fetch_dir, write_dir):
             "source_digest": source_digest(), "kernels": kernels}
 
 
+def mfma(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    agents = glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True)
+    if not files or not agents:
+        raise SystemExit("no counter_collection.csv / agent_info.csv under %s" % d)
+    gpu = [r for r in csv.DictReader(open(agents[0], newline="")) if r.get("Agent_Type") == "GPU"][0]
+    nxcc, nsimd = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    per = defaultdict(dict)
+    for f in files:
+        for r in csv.DictReader(open(f, newline="")):
+            if is_lib(r["Kernel_Name"]):
+                per[(int(r["Dispatch_Id"]), short_name(r["Kernel_Name"]))][r["Counter_Name"]] = \
+                    float(r["Counter_Value"])
+    acc = defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for (_, k), c in per.items():
+        if c.get("SQ_INSTS_MFMA", 0) <= 0:
+            continue
+        a = acc[k]
+        a[0] += 1
+        a[1] += c["SQ_INSTS_MFMA"]
+        a[2] += c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        a[3] += c["GRBM_GUI_ACTIVE"] / nxcc * nsimd
+    lines = ["| kernel | dispatches | MFMA instructions per dispatch | MFMA busy / SIMD-cycles |",
+             "|---|---:|---:|---:|"]
+    for k in sorted(acc):
+        n, ins, busy, avail = acc[k]
+        lines.append("| %s | %d | %.0f | %.1f %% |" % (k, n, ins / n, 100.0 * busy / avail))
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -132,6 +169,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats(a.csv))
+    elif a.cmd == "mfma":
+        print(mfma(a.dir))
     else:
         rec = traffic(a.fetch, a.write)
         txt = json.dumps(rec, indent=1)
