@@ -94,7 +94,14 @@ def mx_quantize_grouped_colwise(x_bf16_bits, offsets):
     32-row block spans two groups.  Returns (codesT uint8 [K, M_pad],
     scalesT uint8 [K, M_pad/32], padded offsets int64 [G+1]).
     """
-    x = np.asarray(x_bf16_bits, dtype=np.uint16)
+    x = bf16_bits_to_f64(np.asarray(x_bf16_bits, dtype=np.uint16))
+    return mx_quantize_grouped_colwise_values(x, offsets)
+
+
+def mx_quantize_grouped_colwise_values(x, offsets):
+    """mx_quantize_grouped_colwise of a float64 matrix [M, K] (any real
+    values, not only BF16 ones): the same padding and blocking."""
+    x = np.asarray(x, dtype=np.float64)
     offsets = np.asarray(offsets, dtype=np.int64)
     K = x.shape[1]
     poff = padded_offsets(offsets)
@@ -106,10 +113,10 @@ def mx_quantize_grouped_colwise(x_bf16_bits, offsets):
         plo, phi = int(poff[g]), int(poff[g + 1])
         if phi == plo:
             continue
-        block = np.zeros((phi - plo, K), np.uint16)   # +0.0 padding rows
+        block = np.zeros((phi - plo, K))              # +0.0 padding rows
         block[: hi - lo] = x[lo:hi]
-        c, s = mx_quantize_colwise(block)
-        codes[:, plo:phi] = c
+        c, s = quantize_blocks(block.T.reshape(K, (phi - plo) // BLOCK, BLOCK))
+        codes[:, plo:phi] = c.reshape(K, phi - plo)
         scales[:, plo // BLOCK: phi // BLOCK] = s
     return codes, scales, poff
 
