@@ -122,6 +122,13 @@ struct GemmArgs {
   void* c; int64_t ldc;
   uint32_t tiles_n;                                 // output tiles along N
   uint32_t nblocks;                                 // grid size (for the XCD remap)
+  // SwiGLU epilogue (variable M): h = silu(gate) * up of the gate/up product,
+  // written as its MX row copy and grouped column copy.
+  int64_t F;                                        // h columns (gate rows per expert)
+  uint8_t* hq; uint8_t* hs; int64_t ldhq, ldhs;     // row copy [M, F], scales [M, F/32]
+  uint8_t* hqT; uint8_t* hsT; int64_t ldhqT, ldhsT; // column copy [F, hcap], scales
+  int64_t hcap;                                     // columns of the column copy
+  int64_t* poff;                                    // padded offsets out [E+1], or null
 };
 
 // One operand of a workgroup: codes and scales as buffer resources whose
@@ -196,6 +203,90 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const OpTile& t) {
   o.s = t.smis + (uint32_t)((e >> 1) * t.lds) + (uint32_t)(e & 1);
   o.sblk = (uint32_t)(e & 1);
   return o;
+}
+
+// SwiGLU product (gate/up weight of one expert: gate rows [0, F), up rows
+// [F, 2F)).  The B stage holds, in LDS row R, for the 64-row block p = R/64,
+// gate row hc0 + 32p + R%32 when R%64 < 32 and the up row F + hc0 + 32p +
+// R%32 otherwise, hc0 being the tile's first h column: each wavefront's 64
+// accumulator columns are then 32 gate columns and the 32 up columns of the
+// same h columns.  -1 marks rows past F.
+__device__ __forceinline__ int64_t gu_row(int R, int64_t hc0, int64_t F) {
+  const int64_t hc = hc0 + 32 * (R >> 6) + (R & 31);
+  if (hc >= F) return -1;
+  return (R & 32) ? F + hc : hc;
+}
+
+// Offset that reads zeros through any descriptor of this file: past every
+// range (ranges stay below 2^30), also after a k offset below 2^31 is added.
+constexpr uint32_t kDeadRow = 0x40000000u;
+
+// A whole expert's gate/up weight as one operand (2F rows from row 0); rows
+// are picked per lane with gu_row.
+__device__ __forceinline__ OpTile op_expert(const uint8_t* q, const uint8_t* s, int64_t ld,
+                                            int64_t lds, int64_t rows, int64_t kdim,
+                                            bool windows) {
+  OpTile t;
+  t.rows = 0;
+  t.ld = (uint32_t)ld;
+  t.lds = (uint32_t)lds;
+  t.q = make_rsrc(q, rows > 0 ? (uint32_t)((rows - 1) * ld + kdim) : 0);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(s);
+  const uintptr_t align = windows ? 15 : 3;
+  t.smis = (uint32_t)(a & align);
+  uint32_t sbytes = rows > 0 ? (uint32_t)((rows - 1) * lds + t.smis + ((kdim + 31) >> 5)) : 0;
+  if (windows) sbytes = (sbytes + 15) & ~15u;
+  t.s = make_rsrc(reinterpret_cast<const uint8_t*>(a & ~align), sbytes);
+  return t;
+}
+
+// lane_offsets for the SwiGLU product's B operand (rows through gu_row).
+__device__ __forceinline__ LaneOffsets lane_offsets_gu(const OpTile& t, int64_t hc0, int64_t F) {
+  LaneOffsets o;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rsub = lane >> 3, slot = lane & 7;
+  o.kc0 = (uint32_t)((slot ^ (rsub >> 1)) * 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t gr = gu_row((w * 4 + j) * 8 + rsub, hc0, F);
+    const uint32_t kc = o.kc0 ^ ((j & 1) * 64);
+    o.q[j] = gr >= 0 ? (uint32_t)(gr * t.ld) + kc : kDeadRow;
+  }
+  const int e = w * 64 + lane;
+  const int64_t gr = gu_row(e >> 1, hc0, F);
+  o.s = gr >= 0 ? t.smis + (uint32_t)(gr * t.lds) + (uint32_t)(e & 1) : kDeadRow;
+  o.sblk = (uint32_t)(e & 1);
+  return o;
+}
+
+// silu(x) = x / (1 + e^-x) in FP32, e^-x = 2^(-x log2 e) on the hardware
+// exponential; for x below about -88 it is +inf and the result -0.
+__device__ __forceinline__ float silu_f32(float x) {
+  const float e = __builtin_amdgcn_exp2f(-x * 1.4426950408889634f);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// MX block of 32 FP32 values: E8M0 code from the largest magnitude (sign
+// cleared, integer order: NaN above Inf above finite values; code = exponent
+// field - 8 clamped at 0, 0xFF for NaN/Inf) and the 32 E4M3 codes packed
+// into 8 dwords (all 0x7F for a NaN/Inf block).
+__device__ __forceinline__ uint32_t mx_block_f32(const float (&v)[32], uint32_t (&out)[8]) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t m = __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu;
+    am = am > m ? am : m;
+  }
+  const uint32_t E = am >> 23;
+  const uint32_t code = am >= 0x7F800000u ? 0xFFu : (E > 8u ? E - 8u : 0u);
+  const float inv = mx_inv_scale(code == 0xFFu ? 127u : code);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    uint32_t w = cvt2_e4m3_sat<false>(v[4 * d] * inv, v[4 * d + 1] * inv, 0u);
+    w = cvt2_e4m3_sat<true>(v[4 * d + 2] * inv, v[4 * d + 3] * inv, w);
+    out[d] = code == 0xFFu ? 0x7F7F7F7Fu : w;
+  }
+  return code;
 }
 
 // The MFMA operand of tile row r for one k-step: 16-byte chunks c0 and c1.
@@ -315,8 +406,11 @@ constexpr int kWinBytes = 2 * TM * 16;
 
 // SW: MX scales read in 16-byte windows (row strides multiples of 16);
 // otherwise byte by byte (any stride).  PT: per-tensor scaled (no block scales).
-template <int KIND, bool PT, int OUT, bool SW>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
+// SWI: the SwiGLU product (variable M, MX): B is an expert's gate/up weight
+// read through gu_row, and the epilogue writes h's MX copies.
+template <int KIND, bool PT, int OUT, bool SW, bool SWI>
+__device__ __forceinline__ void gemm_body(const GemmArgs& g) {
+  static_assert(!SWI || (KIND == kVarM && !PT && OUT == MXQ_OUT_BF16), "SwiGLU product kind");
   constexpr bool SBYTES = !PT && !SW;               // per-step scale-byte loads
   constexpr bool SWIN = !PT && SW;                  // scale windows
   // [slot][A, B] stages; after the k loop, the staged BF16 output tile
@@ -355,6 +449,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
   } else if (KIND == kVarM) {
     group_table(g.offsets, g.E, g.M, s_off, s_start);
+    if (SWI && blockIdx.x == 0 && wave == 0 && g.poff) {
+      // padded offsets of the column copy: each group rounded up to 32 rows
+      int64_t carry = 0;
+      if (lane == 0) g.poff[0] = 0;
+      for (int base = 0; base < g.E; base += 64) {
+        const int gi = base + lane;
+        int64_t v = 0;
+        if (gi < g.E) {
+          const int64_t d = s_off[gi + 1] - s_off[gi];
+          v = d > 0 ? (d + 31) & ~31LL : 0;
+        }
+#pragma unroll
+        for (int sh = 1; sh < 64; sh <<= 1) {
+          const int64_t u = __shfl_up(v, sh, 64);
+          if (lane >= sh) v += u;
+        }
+        if (gi < g.E) g.poff[gi + 1] = carry + v;
+        carry += __shfl(v, 63, 64);
+      }
+    }
     const uint32_t tiles_m = (uint32_t)s_start[g.E];  // data-dependent M-tile count
     const uint32_t tile = blockIdx.x;
     if (tile >= tiles_m * g.tiles_n) return;          // surplus workgroup
@@ -371,8 +485,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
     n0 = (int64_t)tn * TN;
     c_rows = s_off[e + 1] - m0;
     A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
-    B = op_tile(g.b + (int64_t)e * g.b_estride, PT ? nullptr : g.bs + (int64_t)e * g.bs_estride,
-                g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
+    if (SWI)
+      B = op_expert(g.b + (int64_t)e * g.b_estride, g.bs + (int64_t)e * g.bs_estride, g.ldb,
+                    g.ldsb, 2 * g.F, kdim, SW);
+    else
+      B = op_tile(g.b + (int64_t)e * g.b_estride,
+                  PT ? nullptr : g.bs + (int64_t)e * g.bs_estride, g.ldb, g.ldsb, n0, 0,
+                  g.N - n0, kdim, !PT, SW);
   } else {
     // variable K: tile = (e, tm over rows of A = dW rows, tn over rows of B =
     // dW cols).  Work per tile is proportional to the group's tokens, so the
@@ -412,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   const uint32_t kdim32 = (uint32_t)kdim;
   const int32_t nsteps = (int32_t)((kdim + TK - 1) / TK);
   const LaneOffsets oA = lane_offsets(A);
-  const LaneOffsets oB = lane_offsets(B);
+  const LaneOffsets oB = SWI ? lane_offsets_gu(B, n0 / 2, g.F) : lane_offsets(B);
   const i32x4 none = make_rsrc(g.c, 0);              // zero range: loads read 0
   const uint32_t lds_codes = lds_addr(smem), lds_scales = lds_addr(ssc);
 
@@ -463,7 +582,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // slot of window p-1.
   const uint32_t lds_win = lds_scales;
   const int wop = wave >> 2;
-  const uint32_t win_off = (uint32_t)(((wave & 3) * 64 + lane) * (wop ? B.lds : A.lds));
+  uint32_t win_off = (uint32_t)(((wave & 3) * 64 + lane) * (wop ? B.lds : A.lds));
+  if (SWI && wop) {
+    const int64_t gr = gu_row((wave & 3) * 64 + lane, n0 / 2, g.F);
+    win_off = gr >= 0 ? (uint32_t)(gr * B.lds) : kDeadRow;
+  }
   const uint32_t nblk = (kdim32 + 31) >> 5;
   // Only windows holding a block of the range are loaded (the others go
   // through the zero-range descriptor): with an empty range the scale
@@ -622,6 +745,117 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
   // Drain the trailing (zero-range) loads before the LDS goes away.
   wait_vmcnt<0>();
 
+  if constexpr (SWI) {
+    // ---- SwiGLU epilogue: acc[i][0] holds the gate and acc[i][1] the up
+    // values of h columns hb + 8*(v/4) + 4*(lane/32) + v%4 of the tile (hb =
+    // bn/2), rows wm*128 + i*32 + lane%32.
+    const int64_t F = g.F;
+    const int64_t hct = n0 / 2;                     // the tile's first h column
+    const int rows_t = c_rows < TM ? (int)c_rows : TM;
+    const int hb = bn / 2;
+    barrier();                                      // the k loop's LDS reads are done
+    if (cbase) {
+      // The gate/up product in BF16 (gate columns to [hct, +128), up columns
+      // to [F + hct, +128)), staged as [256 rows][128 gate | 128 up].
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ml = wm * 128 + i * 32 + r32, cl = hb + q * 8 + half * 4;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x16& v = acc[i][j];
+            uint2 u;
+            u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 1]) << 16);
+            u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 2]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 3]) << 16);
+            *reinterpret_cast<uint2*>(smem + ml * kCStride + (j * 128 + cl) * 2) = u;
+          }
+        }
+      barrier();
+      const int rsub = lane >> 5, col = lane & 31;
+      const int64_t hc = hct + (col & 15) * 8;
+      const int64_t gcol = ((col >> 4) ? F : 0) + hc;
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int row = wave * 32 + it * 2 + rsub;
+        if (row < rows_t && hc < F) {
+          const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
+          *reinterpret_cast<uint4*>(static_cast<uint8_t*>(cbase) + (m0 + row) * g.ldc * 2 +
+                                    gcol * 2) = v;
+        }
+      }
+      barrier();
+    }
+    // h in FP32, staged as [256 rows][128 columns] (rows of kCStride bytes);
+    // rows past the group are zero: the column copy's padding.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ml = wm * 128 + i * 32 + r32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 hv;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+          hv[e4] = ml < rows_t ? silu_f32(acc[i][0][4 * q + e4]) * acc[i][1][4 * q + e4] : 0.0f;
+        *reinterpret_cast<f32x4*>(smem + ml * kCStride + (hb + q * 8 + half * 4) * 4) = hv;
+      }
+    }
+    barrier();
+    // Row copy: (row, 32-column block) items, two per lane.
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int item = t + kThreads * k;
+      const int row = item >> 2, blk = item & 3;
+      float v[32];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(smem + row * kCStride + blk * 128 + c * 16);
+        v[4 * c] = x[0]; v[4 * c + 1] = x[1]; v[4 * c + 2] = x[2]; v[4 * c + 3] = x[3];
+      }
+      uint32_t w[8];
+      const uint32_t code = mx_block_f32(v, w);
+      const int64_t hc = hct + blk * 32;
+      if (row < rows_t && hc < F) {
+        uint8_t* d = g.hq + (m0 + row) * g.ldhq + hc;
+        *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(d + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        g.hs[(m0 + row) * g.ldhs + (hc >> 5)] = (uint8_t)code;
+      }
+    }
+    // Column copy: (column, 32-row block) items, two per lane, at the
+    // group's padded position.
+    int64_t pe = 0;
+    for (int gi = lane; gi < group; gi += 64) {
+      const int64_t d = s_off[gi + 1] - s_off[gi];
+      pe += d > 0 ? (d + 31) & ~31LL : 0;
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) pe += __shfl_xor(pe, sh, 64);
+    const int64_t pbase = pe + (m0 - s_off[group]);
+    const int rows_p = (rows_t + 31) & ~31;
+    const float* hst = reinterpret_cast<const float*>(smem);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int item = t + kThreads * k;
+      const int col = item & 127, blk = item >> 7;
+      float v[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) v[r] = hst[(blk * 32 + r) * (kCStride / 4) + col];
+      uint32_t w[8];
+      const uint32_t code = mx_block_f32(v, w);
+      const int64_t hc = hct + col, pcol = pbase + blk * 32;
+      if (blk * 32 < rows_p && hc < F && pcol + 32 <= g.hcap) {
+        uint8_t* d = g.hqT + hc * g.ldhqT + pcol;
+        *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(d + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        g.hsT[hc * g.ldhsT + (pcol >> 5)] = (uint8_t)code;
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: acc[i][j] holds C[m = wm*128 + i*32 + lane%32]
   //                [n = bn + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
   float mul = 1.0f;
@@ -677,6 +911,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
       }
     }
   }
+}
+
+template <int KIND, bool PT, int OUT, bool SW>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
+  gemm_body<KIND, PT, OUT, SW, false>(g);
+}
+
+template <bool SW>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_swiglu(GemmArgs g) {
+  gemm_body<kVarM, false, MXQ_OUT_BF16, SW, true>(g);
 }
 
 }  // namespace mxq
@@ -810,6 +1054,59 @@ extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t
   g.offsets = offsets; g.E = E;
   const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
   return launch_gemm<kVarM, false>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
+}
+
+extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, int64_t lda,
+                                      int64_t ldsa, const uint8_t* b, const uint8_t* b_scale,
+                                      int64_t ldb, int64_t ldsb, int64_t b_estride,
+                                      int64_t bs_estride, const int64_t* offsets, int32_t E,
+                                      int64_t M, int64_t F, int64_t K, void* gu, int64_t ldgu,
+                                      uint8_t* hq, int64_t ldhq, uint8_t* hs, int64_t ldhs,
+                                      uint8_t* hqT, int64_t ldhqT, uint8_t* hsT, int64_t ldhsT,
+                                      int64_t M_cap, int64_t* offsets_padded,
+                                      hipStream_t stream) {
+  if (M < 0 || F < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets) return MXQ_ERR_NULL;
+  if (F % 32 != 0 || K % 32 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  if (F == 0) return MXQ_OK;
+  if (M > 0 && (!hq || !hs || (M_cap > 0 && (!hqT || !hsT)))) return MXQ_ERR_NULL;
+  if (ldhq < F || ldhs < F / 32 || ldhqT < M_cap || ldhsT < M_cap / 32) return MXQ_ERR_SHAPE;
+  if (gu && ldgu < 2 * F) return MXQ_ERR_SHAPE;
+  int st;
+  if (K > 0) {
+    // with M == 0 no operand row is read (only the padded offsets are written)
+    if (M > 0 && (st = check_operand(a, a_scale, lda, ldsa, K, true))) return st;
+    if ((st = check_operand(b, b_scale, ldb, ldsb, K, true))) return st;
+  }
+  if (b_estride < 0 || bs_estride < 0) return MXQ_ERR_SHAPE;
+  // One descriptor spans an expert's 2F weight rows.
+  if (2 * F * ldb + K >= (1LL << 30) || 2 * F * ldsb + K / 32 + 16 >= (1LL << 30))
+    return MXQ_ERR_SHAPE;
+  if (b_estride % 16 != 0 || ldhq % 16 != 0 || ldhqT % 16 != 0 || !aligned(hq, 16) ||
+      !aligned(hqT, 16))
+    return MXQ_ERR_ALIGN;
+  if (gu && (ldgu % 8 != 0 || !aligned(gu, 16))) return MXQ_ERR_ALIGN;
+  GemmArgs g = make_args(a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, M, 2 * F, K, gu, ldgu);
+  g.b_estride = b_estride; g.bs_estride = bs_estride;
+  g.offsets = offsets; g.E = E;
+  g.F = F;
+  g.hq = hq; g.hs = hs; g.ldhq = ldhq; g.ldhs = ldhs;
+  g.hqT = hqT; g.hsT = hsT; g.ldhqT = ldhqT; g.ldhsT = ldhsT;
+  g.hcap = M_cap;
+  g.poff = offsets_padded;
+  // Every workgroup past the group tiles exits at once; with M == 0 the first
+  // one still writes the padded offsets.
+  const int64_t blocks = ((M + TM - 1) / TM + E) * (int64_t)g.tiles_n;
+  if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
+  g.nblocks = (uint32_t)blocks;
+  if (ldsa % 16 == 0 && ldsb % 16 == 0)
+    hipLaunchKernelGGL((k_gemm_swiglu<true>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       g);
+  else
+    hipLaunchKernelGGL((k_gemm_swiglu<false>), dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       stream, g);
+  return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 extern "C" int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scales, int64_t lda,

@@ -39,6 +39,10 @@ _SIGS = {
     "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _i32,
                                        _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                        ctypes.c_int, _p]),
+    "mx_grouped_gemm_swiglu": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64,
+                                              _i64, _p, _i32, _i64, _i64, _i64, _p, _i64, _p,
+                                              _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p,
+                                              _p]),
     "fp8_quantize_per_group_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64,
                                                       _i64, _p, _p, _p, _sz, _p]),
     "fp8_grouped_gemm_wgrad_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _p, _i32,
@@ -304,6 +308,45 @@ def mx_grouped_gemm(a, a_scale, b, b_scale, offsets, out_dtype=OUT_BF16,
                                   b.stride(0), b_scale.stride(0), _ptr(offsets), E, M, N, K,
                                   _ptr(c), c.stride(0), out_dtype, accum, _stream()))
     return c
+
+
+def mx_grouped_gemm_swiglu(a, a_scale, b, b_scale, offsets, gu=True, M_cap=None, hq=None,
+                           hs=None, hqT=None, hsT=None, offsets_padded=None):
+    """Gate/up grouped GEMM with SwiGLU and h's MX copies from the epilogue.
+
+    a [M, K] codes with scales [M, K/32] (row copy of the expert inputs);
+    b [E, 2F, K] gate_up codes with scales [E, 2F, K/32] (gate rows first);
+    offsets int64 [E+1] on the device.  ``gu``: True allocates the BF16
+    gate/up product [M, 2F], a tensor receives it, None/False skips it.
+    Returns (gu or None, hq [M, F], hs [M, F/32], hqT [F, M_cap],
+    hsT [F, M_cap/32], offsets_padded [E+1])."""
+    M, K = a.shape
+    E, N2, _ = b.shape
+    F = N2 // 2
+    dev = a.device
+    if M_cap is None:
+        M_cap = colwise_capacity(M, E)
+    if gu is True:
+        gu = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+    elif gu is False:
+        gu = None
+    if hq is None:
+        hq = torch.empty((M, F), dtype=torch.uint8, device=dev)
+    if hs is None:
+        hs = _scale_buffer(M, F // 32, dev)
+    if hqT is None:
+        hqT = torch.empty((F, M_cap), dtype=torch.uint8, device=dev)
+    if hsT is None:
+        hsT = _scale_buffer(F, M_cap // 32, dev)
+    if offsets_padded is None:
+        offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=dev)
+    _check(load().mx_grouped_gemm_swiglu(
+        _ptr(a), _ptr(a_scale), a.stride(0), a_scale.stride(0), _ptr(b), _ptr(b_scale),
+        b.stride(1), b_scale.stride(1), b.stride(0), b_scale.stride(0), _ptr(offsets), E, M, F,
+        K, _ptr(gu), gu.stride(0) if gu is not None else 0, _ptr(hq), hq.stride(0), _ptr(hs),
+        hs.stride(0), _ptr(hqT), hqT.stride(0), _ptr(hsT), hsT.stride(0), M_cap,
+        _ptr(offsets_padded), _stream()))
+    return gu, hq, hs, hqT, hsT, offsets_padded
 
 
 def fp8_grouped_gemm_per_group(a, a_scales, b, b_scales, offsets, out_dtype=OUT_BF16,

@@ -277,6 +277,48 @@ MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t ld
                     hipStream_t stream);
 
 /*
+ * Routed experts' gate/up product with SwiGLU and the MX quantization of its
+ * output in the epilogue (the producer of the down matmul's operands:
+ * [HP329] §5.2 gate_up weight [E, 2F, H] and grouped SwiGLU, §3 row and
+ * column copies; [TTNPU] grouped MX quant for the expert wgrad; [FPBLOG]
+ * §七.2 quantization bookkeeping folded into the producing matmul).
+ *   For each group e with rows [offsets[e], offsets[e+1]):
+ *     GU = A[rows, :] · B_eᵀ  (FP32 sums), g = GU[:, :F], u = GU[:, F:],
+ *     h  = silu(g) * u,  silu(x) = x / (1 + e^-x), in FP32,
+ *   and h is MX-quantized as mx_quantize_dual would quantize it, from the FP32
+ *   values (no BF16 rounding in between).
+ *   a, a_scale  : device, [M, K] codes / [M, K/32] scales (row copy), strides lda, ldsa.
+ *   b, b_scale  : device, per expert e the [2F, K] gate_up codes (gate rows
+ *                 [0, F), up rows [F, 2F)) at b + e*b_estride, row stride ldb,
+ *                 and its scales at b_scale + e*bs_estride, row stride ldsb.
+ *   offsets     : device int64 [E+1] expert row ranges.
+ *   gu          : device BF16 [M, 2F] (row stride ldgu) receiving the gate/up
+ *                 product (for the SwiGLU backward), or NULL to skip it.
+ *   hq, hs      : device, h's row copy: codes [M, F] (stride ldhq), scales
+ *                 [M, F/32] (stride ldhs).
+ *   hqT, hsT    : device, h's grouped column copy: codes [F, M_cap] (stride
+ *                 ldhqT), scales [F, M_cap/32] (stride ldhsT); each group zero-
+ *                 padded to a multiple of 32 rows, as mx_quantize_colwise with
+ *                 offsets; columns past M_cap are not written (M_cap >= M + 31*E
+ *                 holds every padding).
+ *   offsets_padded : device int64 [E+1] receiving the padded offsets, or NULL.
+ * Requires F % 32 == 0, K % 32 == 0, M_cap % 32 == 0, ldhq and ldhqT multiples
+ * of 16 with 16-byte aligned hq, hqT; ldgu % 8 == 0 and 16-byte aligned gu; the
+ * operand requirements of mx_grouped_gemm; an expert's 2F weight rows within
+ * 2^30 bytes.  F == 0 is a no-op; with M == 0 only offsets_padded is written.
+ */
+MXQ_API int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, int64_t lda,
+                           int64_t ldsa, const uint8_t* b, const uint8_t* b_scale,
+                           int64_t ldb, int64_t ldsb, int64_t b_estride, int64_t bs_estride,
+                           const int64_t* offsets, int32_t E,
+                           int64_t M, int64_t F, int64_t K,
+                           void* gu, int64_t ldgu,
+                           uint8_t* hq, int64_t ldhq, uint8_t* hs, int64_t ldhs,
+                           uint8_t* hqT, int64_t ldhqT, uint8_t* hsT, int64_t ldhsT,
+                           int64_t M_cap, int64_t* offsets_padded,
+                           hipStream_t stream);
+
+/*
  * Grouped MX GEMM with variable K (MoE weight gradient, contraction over the
  * tokens of each expert; [HP329] §8 wgrad row, [TTNPU] grouped MX quant for
  * wgrad).  Operands come from mx_quantize_colwise with the same offsets:
@@ -291,6 +333,13 @@ MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t ld
  * Requires lda_t, ldb_t % 16 == 0 and 16-byte aligned code pointers.  As for
  * mx_gemm, scale row strides that are multiples of 16 take the faster path.
  */
+MXQ_API int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t, int64_t ldsa_t,
+                          const uint8_t* bt, const uint8_t* bt_scale, int64_t ldb_t, int64_t ldsb_t,
+                          const int64_t* offsets_padded, int32_t E,
+                          int64_t N, int64_t K,
+                          void* c, int64_t ldc, int out_dtype, int accum,
+                          hipStream_t stream);
+
 /*
  * Grouped FP8 GEMM with per-group FP32 scales, variable M (the grouped
  * matmul of [HP329] §13.4 on operands from fp8_quantize_per_group, [HP329] §3
@@ -327,13 +376,6 @@ MXQ_API int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* a_s
                                      int64_t N, int64_t K,
                                      void* c, int64_t ldc, int out_dtype, int accum,
                                      hipStream_t stream);
-
-MXQ_API int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t, int64_t ldsa_t,
-                          const uint8_t* bt, const uint8_t* bt_scale, int64_t ldb_t, int64_t ldsb_t,
-                          const int64_t* offsets_padded, int32_t E,
-                          int64_t N, int64_t K,
-                          void* c, int64_t ldc, int out_dtype, int accum,
-                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Helpers                                                                   *

@@ -131,3 +131,41 @@ def test_size_limits_rejected(lib):
     # the largest accepted tile stride passes the size check (then fails on alignment)
     ok_ld = ((1 << 31) - 64) // 257 // 16 * 16
     assert lib.mx_gemm(P + 2, P, ok_ld, 64, P, P, 32, 1, 4, 4, 32, P, 4, 0, 0, None) == 3
+
+
+def test_swiglu_product_validation_errors(lib):
+    P = 4096
+    f = lib.mx_grouped_gemm_swiglu
+
+    # (a, as, lda, ldsa, b, bs, ldb, ldsb, b_estride, bs_estride, offsets, E, M, F, K,
+    #  gu, ldgu, hq, ldhq, hs, ldhs, hqT, ldhqT, hsT, ldhsT, M_cap, poff, stream)
+    def call(**kw):
+        a = dict(a=P, as_=P, lda=32, ldsa=16, b=P, bs=P, ldb=32, ldsb=16, be=4096, bse=2048,
+                 off=P, E=4, M=64, F=64, K=32, gu=P, ldgu=128, hq=P, ldhq=64, hs=P, ldhs=16,
+                 hqT=P, ldhqT=256, hsT=P, ldhsT=16, cap=256, poff=P)
+        a.update(kw)
+        return f(a["a"], a["as_"], a["lda"], a["ldsa"], a["b"], a["bs"], a["ldb"], a["ldsb"],
+                 a["be"], a["bse"], a["off"], a["E"], a["M"], a["F"], a["K"], a["gu"],
+                 a["ldgu"], a["hq"], a["ldhq"], a["hs"], a["ldhs"], a["hqT"], a["ldhqT"],
+                 a["hsT"], a["ldhsT"], a["cap"], a["poff"], None)
+
+    assert call(F=40, ldhq=64) == 2                     # F % 32
+    assert call(K=40) == 2                              # K % 32
+    assert call(cap=250) == 2                           # M_cap % 32
+    assert call(off=None) == 1
+    assert call(E=0) == 2
+    assert call(E=257) == 2
+    assert call(hq=None) == 1
+    assert call(hsT=None) == 1
+    assert call(ldhq=48) == 2                           # ldhq < F
+    assert call(ldhq=72) == 3                           # ldhq % 16
+    assert call(ldhqT=264) == 3
+    assert call(ldhqT=224) == 2                         # ldhqT < M_cap
+    assert call(ldgu=96) == 2                           # ldgu < 2F
+    assert call(ldgu=132) == 3                          # ldgu % 8
+    assert call(gu=P + 8) == 3
+    assert call(be=4088) == 3                           # b_estride % 16
+    assert call(lda=24) == 2                            # lda < K
+    # an expert's 2F weight rows must span < 2^30 bytes
+    assert call(F=4096, ldhq=4096, ldgu=8192, ldhs=128, ldb=1 << 17, be=1 << 30) == 2
+    assert call(F=0) == 0                               # no-op
