@@ -264,6 +264,8 @@ def main():
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
     components["per_expert_scaling_step"] = per_expert_step(
         torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
+    components["fused_swiglu_producer"] = fused_producer(
+        torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
     if not args.no_bf16_sweep:
         components["bf16_vs_mx_forward_sweep"] = bf16_sweep(torch, mxq)
         components["bf16_moe_step"] = bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts,
@@ -397,6 +399,75 @@ def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off
     ms = s.elapsed_time(e) / steps
     return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
             "quantization": "per-expert FP32 scales, row-major and transposed copies"}
+
+
+def _timed(torch, fn, *a, reps=5):
+    """Average milliseconds per call of fn over reps calls (two untimed first)."""
+    for _ in range(2):
+        r = fn(*a)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        r = fn(*a)
+    e.record()
+    torch.cuda.synchronize()
+    return r, s.elapsed_time(e) / reps
+
+
+def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops):
+    """The gate/up product with SwiGLU and h's MX row and column copies in
+    its epilogue, against the unfused chain (the product in BF16, SwiGLU,
+    then the dual-axis quantizer on h); and the expert-layer step with the
+    fused producer in place of the product and h's quantization (h is then
+    the SwiGLU of the product instead of a separate input)."""
+    xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(X, offs_d)
+    wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(Wgu, w_off_gu)
+    wv, wsv = wq.view(E, 2 * FFN, HIDDEN), ws.view(E, 2 * FFN, HIDDEN // 32)
+    _, t_fused = _timed(torch, mxq.mx_grouped_gemm_swiglu, xq, xs, wv, wsv, offs_d)
+    _, t_fused_nogu = _timed(torch, lambda: mxq.mx_grouped_gemm_swiglu(xq, xs, wv, wsv, offs_d,
+                                                                       gu=False))
+    gu, t_gemm = _timed(torch, mxq.mx_grouped_gemm, xq, xs, wv, wsv, offs_d)
+    silu = torch.nn.functional.silu
+    hb, t_swiglu = _timed(torch, lambda: silu(gu[:, :FFN]) * gu[:, FFN:])
+    _, t_quant = _timed(torch, mxq.mx_quantize_dual, hb, offs_d)
+
+    def step():
+        gu, hq, hs, hT, hTs, poff_h = mxq.mx_grouped_gemm_swiglu(xq_s[0], xq_s[1], *wgu_s, offs_d)
+        dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(Wdn, w_off_dn)
+        mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
+                            offs_d)
+        gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(dY, offs_d)
+        bq, bs = mxq.expert_view(dnT, dnTs, E, HIDDEN)
+        mxq.mx_grouped_gemm(gq, gs, bq, bs, offs_d)
+        uq, us, duT, duTs, _ = mxq.mx_quantize_dual(dGU, offs_d)
+        bq2, bs2 = mxq.expert_view(wqT_s[0], wqT_s[1], E, 2 * FFN)
+        mxq.mx_grouped_gemm(uq, us, bq2, bs2, offs_d)
+        mxq.mx_grouped_gemm_wgrad(dyT, dyTs, hT, hTs, poff_h)
+        mxq.mx_grouped_gemm_wgrad(duT, duTs, xq_s[2], xq_s[3], poff_h)
+
+    def full_step():
+        # the step's own quantization of X and W_gu, then the rest
+        xq_s[:] = mxq.mx_quantize_dual(X, offs_d)[:4]
+        q = mxq.mx_quantize_dual(Wgu, w_off_gu)
+        wgu_s[:] = [q[0].view(E, 2 * FFN, HIDDEN), q[1].view(E, 2 * FFN, HIDDEN // 32)]
+        wqT_s[:] = [q[2], q[3]]
+        step()
+
+    xq_s, wgu_s, wqT_s = [None] * 4, [None] * 2, [None] * 2
+    _, t_step = _timed(torch, full_step)
+    return {
+        "fused_us": t_fused * 1e3,
+        "fused_without_bf16_product_us": t_fused_nogu * 1e3,
+        "unfused": {"grouped_gemm_us": t_gemm * 1e3, "torch_swiglu_bf16_us": t_swiglu * 1e3,
+                    "dual_quant_h_us": t_quant * 1e3},
+        "saving_vs_gemm_plus_quant_us": (t_gemm + t_quant - t_fused) * 1e3,
+        "step_with_fused_producer": {
+            "ms_per_step": t_step, "TFLOP_per_s_incl_quant": flops / (t_step * 1e-3) / 1e12,
+            "note": "h is the SwiGLU of the gate/up product; no separate h input or its "
+                    "quantization"},
+    }
 
 
 def bf16_sweep(torch, mxq, reps=10):
