@@ -129,6 +129,9 @@ struct GemmArgs {
   uint8_t* hqT; uint8_t* hsT; int64_t ldhqT, ldhsT; // column copy [F, hcap], scales
   int64_t hcap;                                     // columns of the column copy
   int64_t* poff;                                    // padded offsets out [E+1], or null
+  // per-group-scaled SwiGLU product: h in BF16 and each group's max |h|
+  uint16_t* h; int64_t ldh;
+  uint32_t* hamax;                                  // [E] FP32 bit patterns (atomic max)
 };
 
 // One operand of a workgroup: codes and scales as buffer resources whose
@@ -410,7 +413,7 @@ constexpr int kWinBytes = 2 * TM * 16;
 // read through gu_row, and the epilogue writes h's MX copies.
 template <int KIND, bool PT, int OUT, bool SW, bool SWI>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
-  static_assert(!SWI || (KIND == kVarM && !PT && OUT == MXQ_OUT_BF16), "SwiGLU product kind");
+  static_assert(!SWI || (KIND == kVarM && OUT == MXQ_OUT_BF16), "SwiGLU product kind");
   constexpr bool SBYTES = !PT && !SW;               // per-step scale-byte loads
   constexpr bool SWIN = !PT && SW;                  // scale windows
   // [slot][A, B] stages; after the k loop, the staged BF16 output tile
@@ -486,8 +489,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     c_rows = s_off[e + 1] - m0;
     A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
     if (SWI)
-      B = op_expert(g.b + (int64_t)e * g.b_estride, g.bs + (int64_t)e * g.bs_estride, g.ldb,
-                    g.ldsb, 2 * g.F, kdim, SW);
+      B = op_expert(g.b + (int64_t)e * g.b_estride,
+                    PT ? nullptr : g.bs + (int64_t)e * g.bs_estride, g.ldb, g.ldsb, 2 * g.F,
+                    kdim, SW);
     else
       B = op_tile(g.b + (int64_t)e * g.b_estride,
                   PT ? nullptr : g.bs + (int64_t)e * g.bs_estride, g.ldb, g.ldsb, n0, 0,
@@ -753,6 +757,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     const int64_t hct = n0 / 2;                     // the tile's first h column
     const int rows_t = c_rows < TM ? (int)c_rows : TM;
     const int hb = bn / 2;
+    if constexpr (PT) {
+      // per-group scales: the products are scale_a[e] * scale_b[e] * sums
+      const float mul = g.pta[group] * g.ptb[group];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] *= mul;
+    }
     barrier();                                      // the k loop's LDS reads are done
     if (cbase) {
       // The gate/up product in BF16 (gate columns to [hct, +128), up columns
@@ -788,6 +802,53 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
       barrier();
     }
+    if constexpr (PT) {
+      // h in BF16 (the per-group quantizer's input), staged as [256 rows][128
+      // columns], and the group's largest |h| as an FP32 bit pattern
+      // (magnitudes order as integers; NaN above Inf above finite values).
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ml = wm * 128 + i * 32 + r32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t hbits[4];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const float hv = silu_f32(acc[i][0][4 * q + e4]) * acc[i][1][4 * q + e4];
+            hbits[e4] = __builtin_bit_cast(uint16_t, (__bf16)hv);
+          }
+          const bool live = ml < rows_t && hct + hb + q * 8 + half * 4 < F;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const uint32_t m = live ? (hbits[e4] & 0x7FFFu) : 0u;
+            am = am > m ? am : m;
+          }
+          uint2 u;
+          u.x = hbits[0] | (hbits[1] << 16);
+          u.y = hbits[2] | (hbits[3] << 16);
+          *reinterpret_cast<uint2*>(smem + ml * kCStride + (hb + q * 8 + half * 4) * 2) = u;
+        }
+      }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)am, sh, 64);
+        am = am > o ? am : o;
+      }
+      if (lane == 0 && am != 0u) atomicMax(g.hamax + group, am << 16);
+      barrier();
+      const int rsub = lane >> 4, col = lane & 15;
+      const int64_t hc = hct + col * 8;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = wave * 32 + it * 4 + rsub;
+        if (row < rows_t && hc < F) {
+          const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
+          *reinterpret_cast<uint4*>(g.h + (m0 + row) * g.ldh + hc) = v;
+        }
+      }
+      return;
+    } else {
     // h in FP32, staged as [256 rows][128 columns] (rows of kCStride bytes);
     // rows past the group are zero: the column copy's padding.
 #pragma unroll
@@ -854,6 +915,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       }
     }
     return;
+    }
   }
 
   // ---- epilogue: acc[i][j] holds C[m = wm*128 + i*32 + lane%32]
@@ -921,6 +983,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
 template <bool SW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_swiglu(GemmArgs g) {
   gemm_body<kVarM, false, MXQ_OUT_BF16, SW, true>(g);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_swiglu_pg(GemmArgs g) {
+  gemm_body<kVarM, true, MXQ_OUT_BF16, false, true>(g);
+}
+
+__global__ void k_clear_u32(uint32_t* p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 }  // namespace mxq
@@ -1106,6 +1177,48 @@ extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, 
   else
     hipLaunchKernelGGL((k_gemm_swiglu<false>), dim3((uint32_t)blocks), dim3(kThreads), 0,
                        stream, g);
+  return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+extern "C" int fp8_grouped_gemm_per_group_swiglu(const uint8_t* a, const float* a_scales,
+                                                 int64_t lda, const uint8_t* b,
+                                                 const float* b_scales, int64_t ldb,
+                                                 int64_t b_estride, const int64_t* offsets,
+                                                 int32_t E, int64_t M, int64_t F, int64_t K,
+                                                 void* gu, int64_t ldgu, uint16_t* h,
+                                                 int64_t ldh, float* h_amax,
+                                                 hipStream_t stream) {
+  if (M < 0 || F < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets || !a_scales || !b_scales || !h_amax) return MXQ_ERR_NULL;
+  if (F % 32 != 0 || K % 32 != 0) return MXQ_ERR_SHAPE;
+  if (M > 0 && F > 0 && !h) return MXQ_ERR_NULL;
+  if (F > 0 && (ldh < F || (gu && ldgu < 2 * F))) return MXQ_ERR_SHAPE;
+  int st;
+  if (K > 0 && M > 0 && F > 0) {
+    if ((st = check_operand(a, a_scales, lda, 0, K, false))) return st;
+    if ((st = check_operand(b, b_scales, ldb, 0, K, false))) return st;
+  }
+  if (b_estride < 0) return MXQ_ERR_SHAPE;
+  if (2 * F * ldb + K >= (1LL << 30)) return MXQ_ERR_SHAPE;
+  if (b_estride % 16 != 0 || ldh % 8 != 0 || !aligned(h, 16)) return MXQ_ERR_ALIGN;
+  if (gu && (ldgu % 8 != 0 || !aligned(gu, 16))) return MXQ_ERR_ALIGN;
+  // every group's amax starts at zero (also for groups without rows)
+  hipLaunchKernelGGL(k_clear_u32, dim3((uint32_t)((E + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<uint32_t*>(h_amax), E);
+  if (hipGetLastError() != hipSuccess) return MXQ_ERR_HIP;
+  if (M == 0 || F == 0) return MXQ_OK;
+  GemmArgs g = make_args(a, nullptr, lda, 0, b, nullptr, ldb, 0, M, 2 * F, K, gu, ldgu);
+  g.b_estride = b_estride;
+  g.pta = a_scales; g.ptb = b_scales;
+  g.offsets = offsets; g.E = E;
+  g.F = F;
+  g.h = h; g.ldh = ldh;
+  g.hamax = reinterpret_cast<uint32_t*>(h_amax);
+  const int64_t blocks = ((M + TM - 1) / TM + E) * (int64_t)g.tiles_n;
+  if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
+  g.nblocks = (uint32_t)blocks;
+  hipLaunchKernelGGL(k_gemm_swiglu_pg, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, g);
   return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 

@@ -554,6 +554,20 @@ __global__ __launch_bounds__(kPgThreads) void k_pg_scale(const uint32_t* __restr
   }
 }
 
+// Group scales from given group amaxes (FP32, e.g. from the producing
+// matmul's epilogue): the same rule as k_pg_scale; gmax receives the BF16
+// magnitude pattern k_pg_quant tests for NaN/Inf.
+__global__ void k_pg_scale_amax(const float* __restrict__ amax, int32_t E,
+                                uint32_t* __restrict__ gmax, float* __restrict__ scales) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const uint32_t bits = __builtin_bit_cast(uint32_t, amax[e]) & 0x7FFFFFFFu;
+  float sc = 1.0f;
+  if (bits < 0x7F800000u && bits != 0u) sc = __fdiv_rn(__builtin_bit_cast(float, bits), 448.0f);
+  scales[e] = sc;
+  gmax[e] = bits >> 16;
+}
+
 __global__ __launch_bounds__(kPgThreads) void k_pg_quant(const uint16_t* __restrict__ x,
                                                          int64_t M, int64_t K, int64_t ldx,
                                                          const int64_t* __restrict__ offsets,
@@ -710,28 +724,16 @@ extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t a1, int64_t, int
   return 0;
 }
 
-extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                      const int64_t* offsets, int32_t E, uint8_t* q,
-                                      int64_t ldq, float* scales, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
-  if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
-  if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
-  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
-  if (M > 0 && K > 0 && (!x || !q)) return MXQ_ERR_NULL;
-  if (K % 8 != 0) return MXQ_ERR_SHAPE;
-  if (M > 0 && K > 0) {                              // strides of empty inputs are not used
-    if (ldx < K || ldq < K) return MXQ_ERR_SHAPE;
-    if (ldx % 8 != 0 || ldq % 8 != 0 || !aligned(x, 16) || !aligned(q, 8)) return MXQ_ERR_ALIGN;
+// Group scales into scales[E] and the NaN/Inf patterns into gmax: from the
+// given amaxes, or from a row-maxima pass over x (rowmax: M entries).
+static int pg_scales(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     const int64_t* offsets, int32_t E, const float* amax, uint32_t* rowmax,
+                     uint32_t* gmax, float* scales, uint32_t blocks, hipStream_t stream) {
+  if (amax) {
+    hipLaunchKernelGGL(k_pg_scale_amax, dim3((uint32_t)((E + 255) / 256)), dim3(256), 0, stream,
+                       amax, E, gmax, scales);
+    return launch_status();
   }
-  if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
-  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
-    return MXQ_ERR_WORKSPACE;
-  uint32_t* rowmax = static_cast<uint32_t*>(workspace);
-  uint32_t* gmax = rowmax + M;
-  const int64_t waves = (int64_t)num_cus() * 64;    // rows in flight: 16 wavefronts per CU
-  const int64_t rows_blocks = (M + 3) / 4;
-  const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
-                                                             : waves / 4);
   if (M > 0 && K > 0) {
     hipLaunchKernelGGL(k_pg_rowmax, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
                        rowmax);
@@ -743,19 +745,62 @@ extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, i
   if (st != MXQ_OK) return st;
   hipLaunchKernelGGL(k_pg_scale, dim3((uint32_t)E), dim3(kPgThreads), 0, stream, rowmax, offsets,
                      M, gmax, scales);
-  st = launch_status();
+  return launch_status();
+}
+
+static int quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const int64_t* offsets, int32_t E, const float* amax, uint8_t* q,
+                              int64_t ldq, float* scales, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
+  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
+  if (M > 0 && K > 0 && (!x || !q)) return MXQ_ERR_NULL;
+  if (K % 8 != 0) return MXQ_ERR_SHAPE;
+  if (M > 0 && K > 0) {                              // strides of empty inputs are not used
+    if (ldx < K || ldq < K) return MXQ_ERR_SHAPE;
+    if (ldx % 8 != 0 || ldq % 8 != 0 || !aligned(x, 16) || !aligned(q, 8)) return MXQ_ERR_ALIGN;
+  }
+  if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
+  const int64_t ws_rows = amax ? 0 : M;              // row maxima only without amaxes
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, ws_rows, E, 0, 0))
+    return MXQ_ERR_WORKSPACE;
+  uint32_t* rowmax = static_cast<uint32_t*>(workspace);
+  uint32_t* gmax = rowmax + ws_rows;
+  const int64_t waves = (int64_t)num_cus() * 64;    // rows in flight: 16 wavefronts per CU
+  const int64_t rows_blocks = (M + 3) / 4;
+  const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
+                                                             : waves / 4);
+  int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || M == 0 || K == 0) return st;
   hipLaunchKernelGGL(k_pg_quant, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
                      offsets, E, gmax, scales, q, ldq);
   return launch_status();
 }
 
-extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K,
-                                              int64_t ldx, const int64_t* offsets, int32_t E,
-                                              uint8_t* qT, int64_t ldqT, int64_t M_cap,
-                                              float* scales, int64_t* offsets_padded,
-                                              void* workspace, size_t workspace_bytes,
-                                              hipStream_t stream) {
+extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const int64_t* offsets, int32_t E, uint8_t* q,
+                                      int64_t ldq, float* scales, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return quantize_per_group(x, M, K, ldx, offsets, E, nullptr, q, ldq, scales, workspace,
+                            workspace_bytes, stream);
+}
+
+extern "C" int fp8_quantize_per_group_amax(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                           const int64_t* offsets, int32_t E,
+                                           const float* amax, uint8_t* q, int64_t ldq,
+                                           float* scales, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (!amax) return MXQ_ERR_NULL;
+  return quantize_per_group(x, M, K, ldx, offsets, E, amax, q, ldq, scales, workspace,
+                            workspace_bytes, stream);
+}
+
+static int quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                     const int64_t* offsets, int32_t E, const float* amax,
+                                     uint8_t* qT, int64_t ldqT, int64_t M_cap, float* scales,
+                                     int64_t* offsets_padded, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
   if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
@@ -767,26 +812,16 @@ extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int6
       return MXQ_ERR_ALIGN;
   }
   if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
-  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
+  const int64_t ws_rows = amax ? 0 : M;
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, ws_rows, E, 0, 0))
     return MXQ_ERR_WORKSPACE;
   uint32_t* rowmax = static_cast<uint32_t*>(workspace);
-  uint32_t* gmax = rowmax + M;
+  uint32_t* gmax = rowmax + ws_rows;
   const int64_t waves = (int64_t)num_cus() * 64;
   const int64_t rows_blocks = (M + 3) / 4;
   const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
                                                              : waves / 4);
-  if (M > 0 && K > 0) {
-    hipLaunchKernelGGL(k_pg_rowmax, dim3(blocks), dim3(kPgThreads), 0, stream, x, M, K, ldx,
-                       rowmax);
-  } else if (M > 0) {
-    hipLaunchKernelGGL(k_fill_u32, dim3((uint32_t)((M + 255) / 256)), dim3(256), 0, stream,
-                       rowmax, M, 0u);
-  }
-  int st = launch_status();
-  if (st != MXQ_OK) return st;
-  hipLaunchKernelGGL(k_pg_scale, dim3((uint32_t)E), dim3(kPgThreads), 0, stream, rowmax, offsets,
-                     M, gmax, scales);
-  st = launch_status();
+  int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
   const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
   const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
@@ -795,6 +830,27 @@ extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int6
                      x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded,
                      nullptr, 0, nullptr, 0, gmax, scales);
   return launch_status();
+}
+
+extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K,
+                                              int64_t ldx, const int64_t* offsets, int32_t E,
+                                              uint8_t* qT, int64_t ldqT, int64_t M_cap,
+                                              float* scales, int64_t* offsets_padded,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  return quantize_per_group_colwise(x, M, K, ldx, offsets, E, nullptr, qT, ldqT, M_cap, scales,
+                                    offsets_padded, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M, int64_t K,
+                                                   int64_t ldx, const int64_t* offsets,
+                                                   int32_t E, const float* amax, uint8_t* qT,
+                                                   int64_t ldqT, int64_t M_cap, float* scales,
+                                                   int64_t* offsets_padded, void* workspace,
+                                                   size_t workspace_bytes, hipStream_t stream) {
+  if (!amax) return MXQ_ERR_NULL;
+  return quantize_per_group_colwise(x, M, K, ldx, offsets, E, amax, qT, ldqT, M_cap, scales,
+                                    offsets_padded, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,

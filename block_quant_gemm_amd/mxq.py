@@ -43,6 +43,14 @@ _SIGS = {
                                               _i64, _p, _i32, _i64, _i64, _i64, _p, _i64, _p,
                                               _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p,
                                               _p]),
+    "fp8_grouped_gemm_per_group_swiglu": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _p,
+                                                         _i32, _i64, _i64, _i64, _p, _i64, _p,
+                                                         _i64, _p, _p]),
+    "fp8_quantize_per_group_amax": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _p,
+                                                   _i64, _p, _p, _sz, _p]),
+    "fp8_quantize_per_group_colwise_amax": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p,
+                                                           _p, _i64, _i64, _p, _p, _p, _sz,
+                                                           _p]),
     "fp8_quantize_per_group_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64,
                                                       _i64, _p, _p, _p, _sz, _p]),
     "fp8_grouped_gemm_wgrad_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _p, _i32,
@@ -259,6 +267,50 @@ def fp8_quantize_per_group_colwise(x, offsets, M_cap=None, qT=None, scales=None,
     return qT, scales, offsets_padded
 
 
+def fp8_quantize_per_group_amax(x, offsets, amax, q=None, scales=None, workspace=None):
+    """fp8_quantize_per_group with the group amaxes given (float32 [E] on the
+    device, e.g. from fp8_grouped_gemm_per_group_swiglu): no pass over x for
+    them.  Returns (codes uint8 [M, K], scales float32 [E])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = offsets.numel() - 1
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(E, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(WS_PER_GROUP, 0, E), 4), dtype=torch.uint8,
+                                device=x.device)
+    _check(load().fp8_quantize_per_group_amax(_ptr(x), M, K, x.stride(0), _ptr(offsets), E,
+                                              _ptr(amax), _ptr(q), q.stride(0), _ptr(scales),
+                                              _ptr(workspace), workspace.numel(), _stream()))
+    return q, scales
+
+
+def fp8_quantize_per_group_colwise_amax(x, offsets, amax, M_cap=None, qT=None, scales=None,
+                                        offsets_padded=None, workspace=None):
+    """fp8_quantize_per_group_colwise with the group amaxes given.  Returns
+    (codesT uint8 [K, M_cap], scales float32 [E], offsets_padded int64 [E+1])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = offsets.numel() - 1
+    if M_cap is None:
+        M_cap = colwise_capacity(M, E)
+    if qT is None:
+        qT = torch.empty((K, M_cap), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(E, dtype=torch.float32, device=x.device)
+    if offsets_padded is None:
+        offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(WS_PER_GROUP, 0, E), 4), dtype=torch.uint8,
+                                device=x.device)
+    _check(load().fp8_quantize_per_group_colwise_amax(
+        _ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(amax), _ptr(qT), qT.stride(0), M_cap,
+        _ptr(scales), _ptr(offsets_padded), _ptr(workspace), workspace.numel(), _stream()))
+    return qT, scales, offsets_padded
+
+
 # ---------------------------------------------------------------------------
 # GEMMs
 # ---------------------------------------------------------------------------
@@ -347,6 +399,32 @@ def mx_grouped_gemm_swiglu(a, a_scale, b, b_scale, offsets, gu=True, M_cap=None,
         hs.stride(0), _ptr(hqT), hqT.stride(0), _ptr(hsT), hsT.stride(0), M_cap,
         _ptr(offsets_padded), _stream()))
     return gu, hq, hs, hqT, hsT, offsets_padded
+
+
+def fp8_grouped_gemm_per_group_swiglu(a, a_scales, b, b_scales, offsets, gu=True, h=None,
+                                      h_amax=None):
+    """Per-group-scaled gate/up grouped GEMM with SwiGLU in the epilogue.
+
+    a [M, K] and b [E, 2F, K] codes from fp8_quantize_per_group (gate rows
+    first), scales float32 [E].  Returns (gu BF16 [M, 2F] or None, h BF16
+    [M, F], h_amax float32 [E]: each group's largest |h|)."""
+    M, K = a.shape
+    E, N2, _ = b.shape
+    F = N2 // 2
+    dev = a.device
+    if gu is True:
+        gu = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=dev)
+    elif gu is False:
+        gu = None
+    if h is None:
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    if h_amax is None:
+        h_amax = torch.empty(E, dtype=torch.float32, device=dev)
+    _check(load().fp8_grouped_gemm_per_group_swiglu(
+        _ptr(a), _ptr(a_scales), a.stride(0), _ptr(b), _ptr(b_scales), b.stride(1), b.stride(0),
+        _ptr(offsets), E, M, F, K, _ptr(gu), gu.stride(0) if gu is not None else 0, _ptr(h),
+        h.stride(0), _ptr(h_amax), _stream()))
+    return gu, h, h_amax
 
 
 def fp8_grouped_gemm_per_group(a, a_scales, b, b_scales, offsets, out_dtype=OUT_BF16,

@@ -203,6 +203,31 @@ MXQ_API int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t
                                    int64_t* offsets_padded, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fp8_quantize_per_group and fp8_quantize_per_group_colwise with each
+ * group's amax given instead of found by a pass over x ([FPBLOG] §七.2: the
+ * amax pass is current scaling's extra read, and the producing matmul's
+ * epilogue can supply the amax; fp8_grouped_gemm_per_group_swiglu does).
+ *   amax : device float[E], amax[e] = max |x| over group e's rows (NaN if
+ *          the group holds a NaN; 0 for an empty group).  The scale rule is
+ *          the one above applied to amax[e]; the codes equal the plain
+ *          entry's when amax[e] is the group's true max |x|.
+ * The other arguments, layouts and errors are those of the plain entries;
+ * the workspace needs only mxq_workspace_size(MXQ_WS_PER_GROUP, 0, E, 0, 0)
+ * bytes (no row maxima).
+ */
+MXQ_API int fp8_quantize_per_group_amax(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const int64_t* offsets, int32_t E, const float* amax,
+                                uint8_t* q, int64_t ldq, float* scales,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+MXQ_API int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M, int64_t K,
+                                        int64_t ldx, const int64_t* offsets, int32_t E,
+                                        const float* amax, uint8_t* qT, int64_t ldqT,
+                                        int64_t M_cap, float* scales, int64_t* offsets_padded,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * GEMMs                                                                     *
  * ------------------------------------------------------------------------ */
@@ -361,6 +386,34 @@ MXQ_API int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scales, 
                                int64_t M, int64_t N, int64_t K,
                                void* c, int64_t ldc, int out_dtype, int accum,
                                hipStream_t stream);
+
+/*
+ * Per-group-scaled gate/up product with SwiGLU in the epilogue, for the
+ * per-expert current-scaling format ([HP329] §5.2 gate_up [E, 2F, H] and
+ * grouped SwiGLU, §3 per-group scales; [FPBLOG] §七.2 amax taken in the
+ * producing matmul's epilogue):  for each group e with rows
+ * [offsets[e], offsets[e+1]):
+ *   GU = a_scales[e] * b_scales[e] * (Q_a[rows] · Q_b,eᵀ) (FP32),
+ *   h  = BF16(silu(GU[:, :F]) * GU[:, F:])  (silu in FP32, one rounding),
+ *   h_amax[e] = max |h| over the group's rows (0 for an empty group; NaN if
+ *               any h is NaN),
+ * so that fp8_quantize_per_group_amax / _colwise_amax quantize h without an
+ * amax pass.
+ *   a, b        : codes as fp8_grouped_gemm_per_group (b: [2F, K] per expert,
+ *                 gate rows [0, F), up rows [F, 2F)); a_scales, b_scales float[E].
+ *   gu          : device BF16 [M, 2F] (stride ldgu) or NULL.
+ *   h           : device BF16 [M, F], row stride ldh.
+ *   h_amax      : device float[E]; cleared and filled by this call.
+ * Requires F % 32 == 0, K % 32 == 0, ldh % 8 == 0 and 16-byte aligned h; gu
+ * as for mx_grouped_gemm_swiglu; an expert's 2F weight rows within 2^30 bytes.
+ */
+MXQ_API int fp8_grouped_gemm_per_group_swiglu(const uint8_t* a, const float* a_scales,
+                                      int64_t lda, const uint8_t* b, const float* b_scales,
+                                      int64_t ldb, int64_t b_estride,
+                                      const int64_t* offsets, int32_t E,
+                                      int64_t M, int64_t F, int64_t K,
+                                      void* gu, int64_t ldgu, uint16_t* h, int64_t ldh,
+                                      float* h_amax, hipStream_t stream);
 
 /*
  * Weight gradient with per-group FP32 scales (variable K, the per-expert
