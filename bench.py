@@ -457,12 +457,34 @@ def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn,
 
     xq_s, wgu_s, wqT_s = [None] * 4, [None] * 2, [None] * 2
     _, t_step = _timed(torch, full_step)
+
+    # per-expert current scaling: h's group amaxes from the product's epilogue
+    pxq, pxs = mxq.fp8_quantize_per_group(X, offs_d)
+    pwq, pws = mxq.fp8_quantize_per_group(Wgu, w_off_gu)
+    pwv = pwq.view(E, 2 * FFN, HIDDEN)
+    (_, ph, pam), t_pg_fused = _timed(torch, mxq.fp8_grouped_gemm_per_group_swiglu, pxq, pxs,
+                                      pwv, pws, offs_d)
+    _, t_pg_qa = _timed(torch, mxq.fp8_quantize_per_group_amax, ph, offs_d, pam)
+    _, t_pg_qta = _timed(torch, mxq.fp8_quantize_per_group_colwise_amax, ph, offs_d, pam)
+    pgu, t_pg_gemm = _timed(torch, mxq.fp8_grouped_gemm_per_group, pxq, pxs, pwv, pws, offs_d)
+    _, t_pg_q = _timed(torch, mxq.fp8_quantize_per_group, ph, offs_d)
+    _, t_pg_qt = _timed(torch, mxq.fp8_quantize_per_group_colwise, ph, offs_d)
+    pg = {
+        "fused_product_us": t_pg_fused * 1e3,
+        "quant_h_with_amax_us": {"row": t_pg_qa * 1e3, "transposed": t_pg_qta * 1e3},
+        "unfused": {"grouped_gemm_us": t_pg_gemm * 1e3,
+                    "quant_h_us": {"row": t_pg_q * 1e3, "transposed": t_pg_qt * 1e3}},
+        "producer_plus_quant_us": {
+            "fused": (t_pg_fused + t_pg_qa + t_pg_qta) * 1e3,
+            "unfused_without_swiglu": (t_pg_gemm + t_pg_q + t_pg_qt) * 1e3},
+    }
     return {
         "fused_us": t_fused * 1e3,
         "fused_without_bf16_product_us": t_fused_nogu * 1e3,
         "unfused": {"grouped_gemm_us": t_gemm * 1e3, "torch_swiglu_bf16_us": t_swiglu * 1e3,
                     "dual_quant_h_us": t_quant * 1e3},
         "saving_vs_gemm_plus_quant_us": (t_gemm + t_quant - t_fused) * 1e3,
+        "per_expert_scaling": pg,
         "step_with_fused_producer": {
             "ms_per_step": t_step, "TFLOP_per_s_incl_quant": flops / (t_step * 1e-3) / 1e12,
             "note": "h is the SwiGLU of the gate/up product; no separate h input or its "

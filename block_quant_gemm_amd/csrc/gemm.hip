@@ -835,7 +835,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         const uint32_t o = (uint32_t)__shfl_xor((int)am, sh, 64);
         am = am > o ? am : o;
       }
-      if (lane == 0 && am != 0u) atomicMax(g.hamax + group, am << 16);
+      __shared__ uint32_t s_am[kThreads / 64];
+      if (lane == 0) s_am[wave] = am;
       barrier();
       const int rsub = lane >> 4, col = lane & 15;
       const int64_t hc = hct + col * 8;
@@ -846,6 +847,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
           const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
           *reinterpret_cast<uint4*>(g.h + (m0 + row) * g.ldh + hc) = v;
         }
+      }
+      // One atomic per tile, last, so that nothing waits for it (a workgroup
+      // barrier would first complete its round trip to the contended address).
+      if (t == 0) {
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) am = am > s_am[w] ? am : s_am[w];
+        if (am != 0u)
+          __hip_atomic_fetch_max(g.hamax + group, am << 16, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
       return;
     } else {
