@@ -95,6 +95,11 @@ __device__ __forceinline__ void dma_b128(i32x4 r, uint32_t m0, uint32_t off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m), "v"(off), "s"(r) : "memory");
 }
+__device__ __forceinline__ void dma_b32(i32x4 r, uint32_t m0, uint32_t off) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m), "v"(off), "s"(r) : "memory");
+}
 __device__ __forceinline__ void dma_b8(i32x4 r, uint32_t m0, uint32_t off) {
   const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)m0);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
@@ -407,21 +412,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr int kWinSlots = 3;
 constexpr int kWinBytes = 2 * TM * 16;
 
+// Blockwise FP32 scales: per stage (= one 128-wide block of the contraction)
+// 256 A-row scales and the tile's two B block-row scales, [slot][A 256 | B 64].
+constexpr int kBlkScaleWords = 320;
+
 // SW: MX scales read in 16-byte windows (row strides multiples of 16);
 // otherwise byte by byte (any stride).  PT: per-tensor scaled (no block scales).
 // SWI: the SwiGLU product (variable M, MX): B is an expert's gate/up weight
 // read through gu_row, and the epilogue writes h's MX copies.
-template <int KIND, bool PT, int OUT, bool SW, bool SWI>
+// BLK: blockwise FP32 scales (dense only): 1x128 blocks of A, 128x128 blocks
+// of B; each k-step's product is formed with unit scales and promoted into
+// the FP32 accumulators times its blocks' two scales.
+template <int KIND, bool PT, int OUT, bool SW, bool SWI, bool BLK>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   static_assert(!SWI || (KIND == kVarM && OUT == MXQ_OUT_BF16), "SwiGLU product kind");
-  constexpr bool SBYTES = !PT && !SW;               // per-step scale-byte loads
-  constexpr bool SWIN = !PT && SW;                  // scale windows
+  static_assert(!BLK || (KIND == kDense && !PT && !SW && !SWI), "blockwise kind");
+  constexpr bool SBYTES = !PT && !SW && !BLK;       // per-step scale-byte loads
+  constexpr bool SWIN = !PT && SW && !BLK;          // scale windows
   // [slot][A, B] stages; after the k loop, the staged BF16 output tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   // byte path: [slot][k-step][A, B][row][blk] as dwords;
   // windows: [wslot][A, B][row][16 B]
   __shared__ __attribute__((aligned(16)))
-  uint32_t ssc[SBYTES ? kSlots * 2 * 2 * 2 * TM : (SWIN ? kWinSlots * kWinBytes / 4 : 1)];
+  uint32_t ssc[SBYTES ? kSlots * 2 * 2 * 2 * TM
+                      : (SWIN ? kWinSlots * kWinBytes / 4 : (BLK ? kSlots * kBlkScaleWords : 1))];
   __shared__ int64_t s_off[KIND == kVarM ? kMaxGroups + 1 : 1];
   __shared__ int32_t s_start[KIND == kVarM ? kMaxGroups + 1 : 1];
 
@@ -448,8 +462,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     m0 = (int64_t)tm * TM;
     n0 = (int64_t)tn * TN;
     c_rows = g.M - m0;
-    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT, SW);
-    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT, SW);
+    A = op_tile(g.a, g.as, g.lda, g.ldsa, m0, 0, c_rows, kdim, !PT && !BLK, SW);
+    B = op_tile(g.b, g.bs, g.ldb, g.ldsb, n0, 0, g.N - n0, kdim, !PT && !BLK, SW);
   } else if (KIND == kVarM) {
     group_table(g.offsets, g.E, g.M, s_off, s_start);
     if (SWI && blockIdx.x == 0 && wave == 0 && g.poff) {
@@ -523,6 +537,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     cbase = static_cast<uint8_t*>(g.c) + (int64_t)e * g.M * g.ldc * (OUT == MXQ_OUT_FP32 ? 4 : 2);
   }
 
+  // Blockwise scale descriptors: the tile's A rows and B block rows (FP32,
+  // row strides ldsa / ldsb in floats).
+  i32x4 sdA = make_rsrc(g.c, 0), sdB = sdA;
+  if constexpr (BLK) {
+    const int64_t ra = c_rows < TM ? c_rows : TM;
+    const int64_t nbr = (g.N - n0 + 127) / 128 < 2 ? (g.N - n0 + 127) / 128 : 2;
+    const int64_t kb = kdim / 128;
+    sdA = make_rsrc(g.as + m0 * g.ldsa * 4, (uint32_t)(((ra - 1) * g.ldsa + kb) * 4));
+    sdB = make_rsrc(g.bs + (n0 / 128) * g.ldsb * 4, (uint32_t)(((nbr - 1) * g.ldsb + kb) * 4));
+  }
+
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -561,6 +586,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   auto issue_stage_scales = [&](int32_t u) {
     const bool live = u < nstages;
     const uint32_t slot = (uint32_t)(u & (kSlots - 1));
+    if constexpr (BLK) {
+      // waves 0-3: one A-row scale per lane; waves 4-7: the two B block rows
+      // (lanes alternate between them; the copies land on the same words)
+      const uint32_t base = lds_scales + slot * kBlkScaleWords * 4;
+      if (wave < 4) {
+        const i32x4 d = uniform(live ? sdA : none);
+        dma_b32(d, base + wave * 64 * 4,
+                (uint32_t)(((int64_t)(wave * 64 + lane) * g.ldsa + u) * 4));
+      } else {
+        const i32x4 d = uniform(live ? sdB : none);
+        dma_b32(d, base + 256 * 4, (uint32_t)(((int64_t)(lane & 1) * g.ldsb + u) * 4));
+      }
+    }
     if (SBYTES) {
       const i32x4 sa = uniform(live ? A.s : none), sb = uniform(live ? B.s : none);
 #pragma unroll
@@ -618,7 +656,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int i = 0; i < 4; ++i) f.a[i] = read_frag(lA, wm * 128 + i * 32 + r32, c0, c1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) f.b[j] = read_frag(lB, bn + j * 32 + r32, c0, c1);
-    if (PT) {
+    if (BLK) {
+      const uint32_t* sc = ssc + slot * kBlkScaleWords;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.sa[i] = sc[wm * 128 + i * 32 + r32];
+      f.sb[0] = f.sb[1] = sc[256 + (bn >> 7)];
+    } else if (PT) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) f.sa[i] = 127u;
 #pragma unroll
@@ -660,6 +703,32 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     asm volatile("" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),
                  "+v"(f.b[1]), "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]),
                  "+v"(f.sb[0]), "+v"(f.sb[1]));
+    if constexpr (BLK) {
+      // Promotion: each product starts from zero with unit scales, and is
+      // added to the accumulators times sa[row] * sb one MFMA later, so the
+      // adds of one pair overlap the matrix unit's work on the next.
+      float sab[4];
+      const float sbv = __builtin_bit_cast(float, f.sb[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sab[i] = __builtin_bit_cast(float, f.sa[i]) * sbv;
+      const f32x16 zero = {};
+      f32x16 tp[2];
+      static_for<8>([&](auto k) {
+        constexpr int K = decltype(k)::value, i = K / 2, j = K % 2;
+        tp[K & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0,
+                                                                    127, 0, 127);
+        if constexpr (K > 0) {
+          constexpr int P = K - 1, pi = P / 2, pj = P % 2;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acc[pi][pj][v] = __builtin_fmaf(tp[P & 1][v], sab[pi], acc[pi][pj][v]);
+        }
+        if constexpr (ISSUE) stage_dma(u, K);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[3][1][v] = __builtin_fmaf(tp[1][v], sab[3], acc[3][1][v]);
+    } else {
     static_for<8>([&](auto k) {
       constexpr int K = decltype(k)::value, i = K / 2, j = K % 2;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -667,6 +736,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       if constexpr (ISSUE) stage_dma(u, K);
       __builtin_amdgcn_sched_barrier(0);
     });
+    }
     if constexpr (ISSUE) issue_stage_scales(u);
     asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
                  "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]));
@@ -684,7 +754,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     __builtin_amdgcn_sched_barrier(0);
   };
   static_assert(kSlots == 2, "slot reuse below assumes a 2-slot ring");
-  constexpr int VS = vmem_per_stage<SBYTES>();
+  constexpr int VS = BLK ? 9 : vmem_per_stage<SBYTES>();
 
   // Ping-pong.  Each k-step s is a memory phase (read step s's fragments
   // from LDS) and a compute phase (8 MFMAs), separated by workgroup
@@ -987,16 +1057,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 
 template <int KIND, bool PT, int OUT, bool SW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
-  gemm_body<KIND, PT, OUT, SW, false>(g);
+  gemm_body<KIND, PT, OUT, SW, false, false>(g);
 }
 
 template <bool SW>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_swiglu(GemmArgs g) {
-  gemm_body<kVarM, false, MXQ_OUT_BF16, SW, true>(g);
+  gemm_body<kVarM, false, MXQ_OUT_BF16, SW, true, false>(g);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_swiglu_pg(GemmArgs g) {
-  gemm_body<kVarM, true, MXQ_OUT_BF16, false, true>(g);
+  gemm_body<kVarM, true, MXQ_OUT_BF16, false, true, false>(g);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_blockwise(GemmArgs g) {
+  gemm_body<kDense, false, OUT, false, false, true>(g);
 }
 
 __global__ void k_clear_u32(uint32_t* p, int32_t n) {
@@ -1108,6 +1183,39 @@ extern "C" int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64
   g.pta = a_scale; g.ptb = b_scale;
   return launch_gemm<kDense, true>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype,
                                    stream);
+}
+
+extern "C" int fp8_gemm_blockwise(const uint8_t* a, const float* a_scales, int64_t lda,
+                                  int64_t ldsa, const uint8_t* b, const float* b_scales,
+                                  int64_t ldb, int64_t ldsb, int64_t M, int64_t N, int64_t K,
+                                  void* c, int64_t ldc, int out_dtype, int accum,
+                                  hipStream_t stream) {
+  int st = check_common(M, N, K, ldc, out_dtype, accum);
+  if (st) return st;
+  if (K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!c) return MXQ_ERR_NULL;
+  if (K > 0) {
+    if ((st = check_operand(a, a_scales, lda, 0, K, false))) return st;
+    if ((st = check_operand(b, b_scales, ldb, 0, K, false))) return st;
+    if (ldsa < K / 128 || ldsb < K / 128) return MXQ_ERR_SHAPE;
+    // 32-bit scale offsets: a tile's 256 A rows and two B block rows
+    if (ldsa * 4 * (TM + 1) + K >= (1LL << 30) || ldsb * 4 * 3 + K >= (1LL << 30))
+      return MXQ_ERR_SHAPE;
+  }
+  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
+  GemmArgs g = make_args(a, reinterpret_cast<const uint8_t*>(a_scales), lda, ldsa, b,
+                         reinterpret_cast<const uint8_t*>(b_scales), ldb, ldsb, M, N, K, c, ldc);
+  const int64_t blocks = ((M + TM - 1) / TM) * (int64_t)g.tiles_n;
+  if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
+  g.nblocks = (uint32_t)blocks;
+  if (out_dtype == MXQ_OUT_BF16)
+    hipLaunchKernelGGL(k_gemm_blockwise<MXQ_OUT_BF16>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       stream, g);
+  else
+    hipLaunchKernelGGL(k_gemm_blockwise<MXQ_OUT_FP32>, dim3((uint32_t)blocks), dim3(kThreads), 0,
+                       stream, g);
+  return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, int64_t ldsa,

@@ -483,6 +483,110 @@ __global__ __launch_bounds__(kPtThreads) void k_pt_quant(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Blockwise FP8, the comparison recipe ("Transformer 与 LLM（06）：浮点格式、数值
+// 稳定性与混合精度" §七.3, DeepSeek-V3's blocks): one FP32 scale per 1x128
+// activation block or 128x128 weight block, each block quantized by the
+// current-scaling rule (scale = amax / 448, or 1 for a zero or non-finite
+// amax; codes RNE_E4M3(x / scale) with an exact FP32 quotient).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float pt_block_scale(uint32_t m) {
+  return (m < 0x7F80u && m != 0u) ? __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f) : 1.0f;
+}
+
+// 8 BF16 values (one 16-byte load) -> 8 codes with scale s (r = RN(1/s)).
+__device__ __forceinline__ uint2 pt_encode8(uint4 v, float s, float r, bool direct,
+                                            bool nonfinite) {
+  uint32_t lo, hi;
+  if (nonfinite) {
+    lo = pt_nonfinite_pair<false>(v.x, 0u);
+    lo = pt_nonfinite_pair<true>(v.y, lo);
+    hi = pt_nonfinite_pair<false>(v.z, 0u);
+    hi = pt_nonfinite_pair<true>(v.w, hi);
+  } else {
+    lo = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.x), s, r, direct), pt_div(bf16_hi(v.x), s, r, direct), 0u);
+    lo = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.y), s, r, direct), pt_div(bf16_hi(v.y), s, r, direct), lo);
+    hi = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.z), s, r, direct), pt_div(bf16_hi(v.z), s, r, direct), 0u);
+    hi = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.w), s, r, direct), pt_div(bf16_hi(v.w), s, r, direct), hi);
+  }
+  return make_uint2(lo, hi);
+}
+
+constexpr int kDppRowMirror = 0x140;       // lane i <- lane 15 - i within a row of 16
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <- lane 7 - i within each half row
+
+// 1x128 blocks: a wavefront owns 512 consecutive elements of a row (8 per
+// lane), so the 16 lanes of a DPP row hold one block; the block amax is the
+// packed-u16 magnitude max reduced over the row by four DPP exchanges.
+__global__ __launch_bounds__(256) void k_bw_act(const uint16_t* __restrict__ x, int64_t ldx,
+                                                uint8_t* __restrict__ q, int64_t ldq,
+                                                float* __restrict__ sc, int64_t lds, uint32_t K,
+                                                uint32_t segs_per_row, uint32_t total_segs) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
+  for (uint32_t sg = wave; sg < total_segs; sg += nwave) {
+    const uint32_t row = sg / segs_per_row;             // wave-uniform
+    const uint32_t col = (sg - row * segs_per_row) * 512u + lane * 8u;
+    const bool ok = col < K;
+    const uint4 v = ok ? *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + col)
+                       : make_uint4(0, 0, 0, 0);
+    const u16x2 mm = __builtin_elementwise_max(absmax2(v.x, v.y), absmax2(v.z, v.w));
+    uint32_t am = mm.x > mm.y ? mm.x : mm.y;
+    uint32_t o = dpp_u32(am, kQuadXor1);
+    am = am > o ? am : o;
+    o = dpp_u32(am, kQuadXor2);
+    am = am > o ? am : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, kDppRowHalfMirror, 0xF, 0xF, false);
+    am = am > o ? am : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)am, kDppRowMirror, 0xF, 0xF, false);
+    am = am > o ? am : o;
+    const bool nonfinite = am >= 0x7F80u;
+    const float s = pt_block_scale(am);
+    const bool direct = s < 1.17549435e-38f;
+    const uint2 c = pt_encode8(v, s, __frcp_rn(s), direct, nonfinite);
+    if (ok) {
+      store_stream(q + (int64_t)row * ldq + col, c);
+      if ((lane & 15u) == 0u) sc[(int64_t)row * lds + (col >> 7)] = s;
+    }
+  }
+}
+
+// 128x128 blocks: one workgroup per block; lane t holds row t/2 of the block,
+// columns 64*(t%2) .. +63, in registers across the amax reduction.
+__global__ __launch_bounds__(256) void k_bw_weight(const uint16_t* __restrict__ w, int64_t N,
+                                                   int64_t ldw, uint8_t* __restrict__ q,
+                                                   int64_t ldq, float* __restrict__ sc,
+                                                   int64_t lds, uint32_t kblocks) {
+  __shared__ uint32_t red[4];
+  const uint32_t rb = blockIdx.x / kblocks, kb = blockIdx.x - rb * kblocks;
+  const int64_t row = (int64_t)rb * 128 + (threadIdx.x >> 1);
+  const int64_t col = (int64_t)kb * 128 + (threadIdx.x & 1u) * 64;
+  const bool ok = row < N;
+  uint4 v[8];
+  uint32_t am = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    v[u] = ok ? *reinterpret_cast<const uint4*>(w + row * ldw + col + 8 * u)
+              : make_uint4(0, 0, 0, 0);
+    const u16x2 mm = __builtin_elementwise_max(absmax2(v[u].x, v[u].y), absmax2(v[u].z, v[u].w));
+    const uint32_t t = mm.x > mm.y ? mm.x : mm.y;
+    am = am > t ? am : t;
+  }
+  am = block_max_u32(am, red);
+  const bool nonfinite = am >= 0x7F80u;
+  const float s = pt_block_scale(am);
+  const bool direct = s < 1.17549435e-38f;
+  const float r = __frcp_rn(s);
+  if (ok) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      store_stream(q + row * ldq + col + 8 * u, pt_encode8(v[u], s, r, direct, nonfinite));
+  }
+  if (threadIdx.x == 0) sc[(int64_t)rb * lds + kb] = s;
+}
+
 __global__ void k_fill_f32(float* p, float v) {
   if (threadIdx.x == 0) *p = v;
 }
@@ -876,5 +980,46 @@ extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q,
   if (st != MXQ_OK) return st;
   hipLaunchKernelGGL(k_pt_quant, dim3((uint32_t)blocks), dim3(kPtThreads), 0, stream, x, n,
                      partial, (int)blocks, q, scale);
+  return launch_status();
+}
+
+extern "C" int fp8_quantize_blockwise_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                          uint8_t* q, int64_t ldq, float* scales, int64_t lds,
+                                          hipStream_t stream) {
+  if (M < 0 || K < 0 || K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return MXQ_OK;
+  if (!x || !q || !scales) return MXQ_ERR_NULL;
+  if (ldx < K || ldq < K || lds < K / 128) return MXQ_ERR_SHAPE;
+  if (ldx % 8 != 0 || ldq % 8 != 0 || !aligned(x, 16) || !aligned(q, 8) || !aligned(scales, 4))
+    return MXQ_ERR_ALIGN;
+  // A contiguous matrix is one long row (blocks never cross row ends: K % 128 == 0).
+  int64_t rows = M, cols = K;
+  if (ldx == K && ldq == K && lds == K / 128 && M * K <= 0xFFFFFFFFLL) { rows = 1; cols = M * K; }
+  const int64_t segs_per_row = (cols + 511) / 512;
+  const int64_t total = rows * segs_per_row;
+  if (cols > 0xFFFFFFFFLL || total > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  int64_t blocks = (total + 3) / 4;
+  const int64_t cap = (int64_t)num_cus() * 16;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(k_bw_act, dim3((uint32_t)blocks), dim3(256), 0, stream, x,
+                     rows == 1 ? cols : ldx, q, rows == 1 ? cols : ldq, scales,
+                     rows == 1 ? cols / 128 : lds, (uint32_t)cols, (uint32_t)segs_per_row,
+                     (uint32_t)total);
+  return launch_status();
+}
+
+extern "C" int fp8_quantize_blockwise_weight(const uint16_t* w, int64_t N, int64_t K,
+                                             int64_t ldw, uint8_t* q, int64_t ldq,
+                                             float* scales, int64_t lds, hipStream_t stream) {
+  if (N < 0 || K < 0 || K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (N == 0 || K == 0) return MXQ_OK;
+  if (!w || !q || !scales) return MXQ_ERR_NULL;
+  if (ldw < K || ldq < K || lds < K / 128) return MXQ_ERR_SHAPE;
+  if (ldw % 8 != 0 || ldq % 8 != 0 || !aligned(w, 16) || !aligned(q, 8) || !aligned(scales, 4))
+    return MXQ_ERR_ALIGN;
+  const int64_t nblocks = ((N + 127) / 128) * (K / 128);
+  if (nblocks > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  hipLaunchKernelGGL(k_bw_weight, dim3((uint32_t)nblocks), dim3(256), 0, stream, w, N, ldw, q,
+                     ldq, scales, lds, (uint32_t)(K / 128));
   return launch_status();
 }

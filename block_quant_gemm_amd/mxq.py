@@ -51,6 +51,11 @@ _SIGS = {
     "fp8_quantize_per_group_colwise_amax": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p,
                                                            _p, _i64, _i64, _p, _p, _p, _sz,
                                                            _p]),
+    "fp8_quantize_blockwise_act": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "fp8_quantize_blockwise_weight": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                                     _p]),
+    "fp8_gemm_blockwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64,
+                                          _i64, _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
     "fp8_quantize_per_group_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64,
                                                       _i64, _p, _p, _p, _sz, _p]),
     "fp8_grouped_gemm_wgrad_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _p, _i32,
@@ -399,6 +404,46 @@ def mx_grouped_gemm_swiglu(a, a_scale, b, b_scale, offsets, gu=True, M_cap=None,
         hs.stride(0), _ptr(hqT), hqT.stride(0), _ptr(hsT), hsT.stride(0), M_cap,
         _ptr(offsets_padded), _stream()))
     return gu, hq, hs, hqT, hsT, offsets_padded
+
+
+def fp8_quantize_blockwise_act(x, q=None, scales=None):
+    """1x128 blockwise E4M3 of a BF16 [M, K] matrix (K % 128 == 0).
+    Returns (codes uint8 [M, K], scales float32 [M, K/128])."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _check(load().fp8_quantize_blockwise_act(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0),
+                                             _ptr(scales), scales.stride(0), _stream()))
+    return q, scales
+
+
+def fp8_quantize_blockwise_weight(w, q=None, scales=None):
+    """128x128 blockwise E4M3 of a BF16 [N, K] weight (K % 128 == 0).
+    Returns (codes uint8 [N, K], scales float32 [ceil(N/128), K/128])."""
+    w = _bf16_bits(w)
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(((N + 127) // 128, K // 128), dtype=torch.float32, device=w.device)
+    _check(load().fp8_quantize_blockwise_weight(_ptr(w), N, K, w.stride(0), _ptr(q), q.stride(0),
+                                                _ptr(scales), scales.stride(0), _stream()))
+    return q, scales
+
+
+def fp8_gemm_blockwise(a, a_scales, b, b_scales, out_dtype=OUT_BF16, accum=ACC_MFMA_FP8,
+                       c=None):
+    """C = A·Bᵀ on blockwise operands (1x128 A blocks, 128x128 B blocks)."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = _out(M, N, out_dtype, a.device, c)
+    _check(load().fp8_gemm_blockwise(_ptr(a), _ptr(a_scales), a.stride(0), a_scales.stride(0),
+                                     _ptr(b), _ptr(b_scales), b.stride(0), b_scales.stride(0),
+                                     M, N, K, _ptr(c), c.stride(0), out_dtype, accum, _stream()))
+    return c
 
 
 def fp8_grouped_gemm_per_group_swiglu(a, a_scales, b, b_scales, offsets, gu=True, h=None,

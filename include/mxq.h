@@ -275,6 +275,46 @@ MXQ_API int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64_t 
                         hipStream_t stream);
 
 /*
+ * Blockwise FP8, the comparison recipe ([FPBLOG] §七.3, DeepSeek-V3): E4M3
+ * codes with one FP32 scale per 1x128 activation block (per row, per 128
+ * columns) or 128x128 weight block, each block quantized by the current-
+ * scaling rule of fp8_quantize_per_tensor (scale = amax/448 in FP32 if amax
+ * is finite and > 0, else 1.0; codes RNE_E4M3(fp32(x)/scale), saturating).
+ *   x, w    : device BF16 [M, K] / [N, K], row strides ldx / ldw (multiples
+ *             of 8), 16-byte aligned; K % 128 == 0.
+ *   q       : device E4M3 codes, same shape, row stride ldq (multiple of 8).
+ *   scales  : device float, activations [M, K/128], weights [ceil(N/128),
+ *             K/128] (the last block row may cover fewer than 128 rows), row
+ *             stride lds (floats).
+ */
+MXQ_API int fp8_quantize_blockwise_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* q, int64_t ldq, float* scales, int64_t lds,
+                               hipStream_t stream);
+MXQ_API int fp8_quantize_blockwise_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* q, int64_t ldq, float* scales, int64_t lds,
+                                  hipStream_t stream);
+
+/*
+ * Blockwise FP8 GEMM ([FPBLOG] §七.3: each 128-wide slice of the contraction
+ * is multiplied by its blocks' s_a * s_w when it is promoted into the FP32
+ * sum):  C[m, n] = Σ_b a_scales[m, b] * b_scales[n/128, b] * Σ_{k in block b} Q_a[m,k] Q_b[n,k].
+ * Each 64-wide half of a block is formed on the FP8 matrix unit with unit
+ * scales and added to the FP32 accumulators times the two scales (FMA).
+ *   a, a_scales : codes [M, K] (lda) and float [M, K/128] (ldsa, floats),
+ *                 from fp8_quantize_blockwise_act.
+ *   b, b_scales : codes [N, K] (ldb) and float [ceil(N/128), K/128] (ldsb),
+ *                 from fp8_quantize_blockwise_weight.
+ *   c           : device [M, N] BF16 or FP32, row stride ldc.
+ * Requires K % 128 == 0, lda/ldb multiples of 16 with 16-byte aligned codes,
+ * 4-byte aligned scales.
+ */
+MXQ_API int fp8_gemm_blockwise(const uint8_t* a, const float* a_scales, int64_t lda, int64_t ldsa,
+                       const uint8_t* b, const float* b_scales, int64_t ldb, int64_t ldsb,
+                       int64_t M, int64_t N, int64_t K,
+                       void* c, int64_t ldc, int out_dtype, int accum,
+                       hipStream_t stream);
+
+/*
  * Grouped MX GEMM with variable M (MoE forward and dgrad; [HP329] §5.2
  * routed experts, §13.4 low_precision_grouped_matmul with group_list;
  * [TTNPU] grouped matmul).
