@@ -346,6 +346,17 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
     (px, sx), t_px = timed(mxq.fp8_quantize_per_tensor, X)
     (pw, sw), t_pw = timed(mxq.fp8_quantize_per_tensor, W)
     _, t_pg = timed(mxq.fp8_gemm_per_tensor, px, sx, pw, sw)
+    (bx, bsx), t_bx = timed(mxq.fp8_quantize_blockwise_act, X)
+    (bwq, bsw), t_bw = timed(mxq.fp8_quantize_blockwise_weight, W)
+    _, t_bg = timed(mxq.fp8_gemm_blockwise, bx, bsx, bwq, bsw)
+    # output error of each format against the FP32 product of the BF16 inputs
+    ref = X.float() @ W.float().t()
+    rn = ref.norm().item()
+    rel = lambda c: ((c.float() - ref).norm().item() / rn)
+    errs = {"mx": rel(mxq.mx_gemm(xq, xs, wq, ws)),
+            "per_tensor": rel(mxq.fp8_gemm_per_tensor(px, sx, pw, sw)),
+            "blockwise": rel(mxq.fp8_gemm_blockwise(bx, bsx, bwq, bsw))}
+    del ref
     gb = lambda n, b, ms: n * b / (ms * 1e-3) / 1e9
     return {
         "shape": "X 8192x2048, W 10944x2048",
@@ -355,6 +366,10 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "per_tensor_quant_X": {"us": t_px * 1e3, "GB_per_s_algorithmic": gb(nX, 3, t_px)},
         "per_tensor_quant_W": {"us": t_pw * 1e3, "GB_per_s_algorithmic": gb(nW, 3, t_pw)},
         "per_tensor_gemm_fwd": {"us": t_pg * 1e3, "TFLOP_per_s": flops / (t_pg * 1e-3) / 1e12},
+        "blockwise_quant_X_1x128": {"us": t_bx * 1e3, "GB_per_s": gb(nX, 3 + 4 / 128, t_bx)},
+        "blockwise_quant_W_128x128": {"us": t_bw * 1e3, "GB_per_s": gb(nW, 3, t_bw)},
+        "blockwise_gemm_fwd": {"us": t_bg * 1e3, "TFLOP_per_s": flops / (t_bg * 1e-3) / 1e12},
+        "relative_output_error_vs_fp32_of_bf16_inputs": errs,
     }
 
 
