@@ -349,6 +349,21 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
     (bx, bsx), t_bx = timed(mxq.fp8_quantize_blockwise_act, X)
     (bwq, bsw), t_bw = timed(mxq.fp8_quantize_blockwise_weight, W)
     _, t_bg = timed(mxq.fp8_gemm_blockwise, bx, bsx, bwq, bsw)
+    # the vendor library's per-tensor FP8 GEMM (hipBLASLt through torch) on the
+    # same codes and scales: run-only context, and a cross-check of ours
+    vendor = None
+    try:
+        f8 = torch.float8_e4m3fn
+        vend = lambda: torch._scaled_mm(px.view(f8), pw.view(f8).t(), scale_a=sx.reshape(()),
+                                        scale_b=sw.reshape(()), out_dtype=torch.bfloat16)
+        cv, t_v = timed(vend)
+        ours = mxq.fp8_gemm_per_tensor(px, sx, pw, sw)
+        vendor = {"per_tensor_gemm_fwd_us": t_v * 1e3,
+                  "TFLOP_per_s": flops / (t_v * 1e-3) / 1e12,
+                  "max_abs_diff_vs_ours_over_max_abs": (
+                      (cv.float() - ours.float()).abs().max() / cv.float().abs().max()).item()}
+    except (RuntimeError, AttributeError) as ex:        # not built into this torch
+        vendor = {"unavailable": str(ex).splitlines()[0][:200]}
     # output error of each format against the FP32 product of the BF16 inputs
     ref = X.float() @ W.float().t()
     rn = ref.norm().item()
@@ -370,6 +385,7 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "blockwise_quant_W_128x128": {"us": t_bw * 1e3, "GB_per_s": gb(nW, 3, t_bw)},
         "blockwise_gemm_fwd": {"us": t_bg * 1e3, "TFLOP_per_s": flops / (t_bg * 1e-3) / 1e12},
         "relative_output_error_vs_fp32_of_bf16_inputs": errs,
+        "vendor_hipblaslt_per_tensor_fp8": vendor,
     }
 
 
