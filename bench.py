@@ -58,6 +58,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
+    ap.add_argument("--step-only", action="store_true",
+                    help="only the expert-layer step (no dense, per-expert, fused or BF16 "
+                         "components), e.g. for counter passes")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize each tensor with separate row-wise and column-wise passes")
     ap.add_argument("--no-bf16-sweep", action="store_true",
@@ -260,13 +263,14 @@ def main():
                   "gemm_only_TFLOP_per_s": flops / (gemm_ms * 1e-3) / 1e12,
                   "quant_only_GB_per_s": quant_bytes / (quant_ms * 1e-3) / 1e9,
                   "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
-    if not args.no_dense:
+    if not args.no_dense and not args.step_only:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
-    components["per_expert_scaling_step"] = per_expert_step(
-        torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
-    components["fused_swiglu_producer"] = fused_producer(
-        torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
-    if not args.no_bf16_sweep:
+    if not args.step_only:
+        components["per_expert_scaling_step"] = per_expert_step(
+            torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
+        components["fused_swiglu_producer"] = fused_producer(
+            torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
+    if not args.no_bf16_sweep and not args.step_only:
         components["bf16_vs_mx_forward_sweep"] = bf16_sweep(torch, mxq)
         components["bf16_moe_step"] = bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts,
                                                     ms_step)
