@@ -553,23 +553,26 @@ __global__ __launch_bounds__(256) void k_bw_act(const uint16_t* __restrict__ x, 
   }
 }
 
-// 128x128 blocks: one workgroup per block; lane t holds row t/2 of the block,
-// columns 64*(t%2) .. +63, in registers across the amax reduction.
+// 128x128 blocks: one workgroup per block, held in registers across its amax
+// reduction.  Each load instruction of a wavefront reads 4 whole 256-byte
+// block rows (16 lanes per row); a lane's 8 loads are rows 32w + 4u + t/16,
+// u = 0..7, of wavefront w, all at columns 8 (t%16) .. +7.
 __global__ __launch_bounds__(256) void k_bw_weight(const uint16_t* __restrict__ w, int64_t N,
                                                    int64_t ldw, uint8_t* __restrict__ q,
                                                    int64_t ldq, float* __restrict__ sc,
                                                    int64_t lds, uint32_t kblocks) {
   __shared__ uint32_t red[4];
   const uint32_t rb = blockIdx.x / kblocks, kb = blockIdx.x - rb * kblocks;
-  const int64_t row = (int64_t)rb * 128 + (threadIdx.x >> 1);
-  const int64_t col = (int64_t)kb * 128 + (threadIdx.x & 1u) * 64;
-  const bool ok = row < N;
+  const uint32_t lane = threadIdx.x & 63u, wv = threadIdx.x >> 6;
+  const int64_t row0 = (int64_t)rb * 128 + wv * 32 + (lane >> 4);
+  const int64_t col = (int64_t)kb * 128 + (lane & 15u) * 8;
   uint4 v[8];
   uint32_t am = 0;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    v[u] = ok ? *reinterpret_cast<const uint4*>(w + row * ldw + col + 8 * u)
-              : make_uint4(0, 0, 0, 0);
+    const int64_t row = row0 + 4 * u;
+    v[u] = row < N ? *reinterpret_cast<const uint4*>(w + row * ldw + col)
+                   : make_uint4(0, 0, 0, 0);
     const u16x2 mm = __builtin_elementwise_max(absmax2(v[u].x, v[u].y), absmax2(v[u].z, v[u].w));
     const uint32_t t = mm.x > mm.y ? mm.x : mm.y;
     am = am > t ? am : t;
@@ -579,10 +582,10 @@ __global__ __launch_bounds__(256) void k_bw_weight(const uint16_t* __restrict__ 
   const float s = pt_block_scale(am);
   const bool direct = s < 1.17549435e-38f;
   const float r = __frcp_rn(s);
-  if (ok) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      store_stream(q + row * ldq + col + 8 * u, pt_encode8(v[u], s, r, direct, nonfinite));
+  for (int u = 0; u < 8; ++u) {
+    const int64_t row = row0 + 4 * u;
+    if (row < N) store_stream(q + row * ldq + col, pt_encode8(v[u], s, r, direct, nonfinite));
   }
   if (threadIdx.x == 0) sc[(int64_t)rb * lds + kb] = s;
 }
