@@ -263,6 +263,8 @@ def main():
                   "gemm_only_TFLOP_per_s": flops / (gemm_ms * 1e-3) / 1e12,
                   "quant_only_GB_per_s": quant_bytes / (quant_ms * 1e-3) / 1e9,
                   "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
+    if not args.step_only:
+        components["step_as_hip_graph"] = graph_step(torch, step, flops, args.steps)
     if not args.no_dense and not args.step_only:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
     if not args.step_only:
@@ -434,6 +436,30 @@ def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off
     ms = s.elapsed_time(e) / steps
     return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
             "quantization": "per-expert FP32 scales, row-major and transposed copies"}
+
+
+def graph_step(torch, step, flops, steps):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph; the
+    library only enqueues kernels on the current stream) and replayed: the
+    host-side launch cost of its 12 launches leaves the step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12}
 
 
 def _timed(torch, fn, *a, reps=5):
