@@ -530,7 +530,35 @@ def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn,
     pgu, t_pg_gemm = _timed(torch, mxq.fp8_grouped_gemm_per_group, pxq, pxs, pwv, pws, offs_d)
     _, t_pg_q = _timed(torch, mxq.fp8_quantize_per_group, ph, offs_d)
     _, t_pg_qt = _timed(torch, mxq.fp8_quantize_per_group_colwise, ph, offs_d)
+    def pg_step():
+        # the per-expert-scaling step with the fused producer: h's group amaxes
+        # come from the gate/up epilogue
+        xq, xs = mxq.fp8_quantize_per_group(X, offs_d)
+        wq, ws = mxq.fp8_quantize_per_group(Wgu, w_off_gu)
+        _, hb, ham = mxq.fp8_grouped_gemm_per_group_swiglu(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                                                          ws, offs_d)
+        hq, hs = mxq.fp8_quantize_per_group_amax(hb, offs_d, ham)
+        dq, dsc = mxq.fp8_quantize_per_group(Wdn, w_off_dn)
+        mxq.fp8_grouped_gemm_per_group(hq, hs, dq.view(E, HIDDEN, FFN), dsc, offs_d)
+        gq, gs = mxq.fp8_quantize_per_group(dY, offs_d)
+        dnT, dnTs, _ = mxq.fp8_quantize_per_group_colwise(Wdn, w_off_dn)
+        mxq.fp8_grouped_gemm_per_group(
+            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dnTs, offs_d)
+        uq, us = mxq.fp8_quantize_per_group(dGU, offs_d)
+        guT, guTs, _ = mxq.fp8_quantize_per_group_colwise(Wgu, w_off_gu)
+        mxq.fp8_grouped_gemm_per_group(
+            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), guTs, offs_d)
+        dyT, dyTs, poff = mxq.fp8_quantize_per_group_colwise(dY, offs_d)
+        hT, hTs, _ = mxq.fp8_quantize_per_group_colwise_amax(hb, offs_d, ham)
+        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, dyTs, hT, hTs, poff)
+        duT, duTs, _ = mxq.fp8_quantize_per_group_colwise(dGU, offs_d)
+        xT, xTs, _ = mxq.fp8_quantize_per_group_colwise(X, offs_d)
+        mxq.fp8_grouped_gemm_wgrad_per_group(duT, duTs, xT, xTs, poff)
+
+    _, t_pg_step = _timed(torch, pg_step)
     pg = {
+        "step_with_fused_producer": {
+            "ms_per_step": t_pg_step, "TFLOP_per_s_incl_quant": flops / (t_pg_step * 1e-3) / 1e12},
         "fused_product_us": t_pg_fused * 1e3,
         "quant_h_with_amax_us": {"row": t_pg_qa * 1e3, "transposed": t_pg_qta * 1e3},
         "unfused": {"grouped_gemm_us": t_pg_gemm * 1e3,
