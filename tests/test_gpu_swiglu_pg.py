@@ -14,7 +14,6 @@ import pytest
 
 from block_quant_gemm_amd import mxq, workloads
 from oracle import codec, gemm, per_tensor
-from oracle import swiglu as sw
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 from tests.test_gpu_per_group import _gemm_allowance
 from tests.test_gpu_swiglu import h_bounds
@@ -131,3 +130,52 @@ def test_per_group_swiglu_product(counts, F, K):
     t2 = mxq.fp8_quantize_per_group_colwise(h, offs_d)
     for x1, x2 in zip(t1, t2):
         assert np.array_equal(host(x1), host(x2))
+
+
+def test_per_group_swiglu_full_size_sampled():
+    """The per-group-scaled gate/up product with SwiGLU at full size (49152
+    rows, 64 Zipf experts, F 1408, K 2048; operands from the per-group
+    quantizer, whose codes and scales are pinned bit-exact to the oracle in
+    tests/test_gpu_per_group.py): 1500 sampled h values within their intervals,
+    600 sampled gate/up outputs, and every group's amax equal to the max |h|
+    the kernel wrote."""
+    say("per-group SwiGLU product 49152 x (2 x 1408) x 2048, 64 experts")
+    d = workloads.moe_forward(0)
+    offs, E, F, K = d["offsets"], 64, workloads.MOE_FFN, workloads.HIDDEN
+    woffs = np.arange(E + 1, dtype=np.int64) * 2 * F
+    offs_d = to_dev(offs)
+    aq, sa = mxq.fp8_quantize_per_group(to_dev_bf16(d["X"]), offs_d)
+    wq, wsc = mxq.fp8_quantize_per_group(to_dev_bf16(d["W_gu"].reshape(E * 2 * F, K)),
+                                         to_dev(woffs))
+    gu, h, h_amax = mxq.fp8_grouped_gemm_per_group_swiglu(aq, sa, wq.view(E, 2 * F, K), wsc,
+                                                          offs_d)
+    ah, sah, wh, swh = host(aq), host(sa), host(wq), host(wsc)
+    guh, hv, amh = host(gu), codec.bf16_bits_to_f64(host(h)), host(h_amax)
+    rng = np.random.default_rng(13)
+    M = ah.shape[0]
+
+    def ref(rows, wrows):
+        e = np.searchsorted(offs, rows, side="right") - 1
+        idx = np.arange(len(rows))
+        A = per_tensor.pt_dequantize(ah[rows], np.float32(1.0)) * sah[e].astype(np.float64)[:, None]
+        B = per_tensor.pt_dequantize(wh[wrows], np.float32(1.0)) * swh[e].astype(np.float64)[:, None]
+        Y, S = gemm.gemm_ref_entries(A, B, idx, idx)
+        ones = np.full((len(rows), K // 32), 127, np.uint8)
+        T = gemm.fp8_mfma_truncation_bound(ah[rows], ones, wh[wrows], ones, idx, idx) * \
+            sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y)
+        return Y, gemm.tolerance(S) + T, S, T
+
+    r, n = rng.integers(0, M, 600), rng.integers(0, 2 * F, 600)
+    e = np.searchsorted(offs, r, side="right") - 1
+    Y, _, S, T = ref(r, e * 2 * F + n)
+    assert gemm.check_bf16_extra(guh[r, n], Y, S, T).all()
+    r, c = rng.integers(0, M, 1500), rng.integers(0, F, 1500)
+    e = np.searchsorted(offs, r, side="right") - 1
+    g, dg, _, _ = ref(r, e * 2 * F + c)
+    u, du, _, _ = ref(r, e * 2 * F + F + c)
+    lo, hi = h_bounds(g, u, dg, du)
+    ok = (hv[r, c] >= codec.bf16_round(lo)) & (hv[r, c] <= codec.bf16_round(hi))
+    assert ok.all()
+    for k in range(E):
+        a, b = int(offs[k]), int(offs[k + 1])
+        assert amh[k] == (np.max(np.abs(hv[a:b])) if b > a else 0.0)
