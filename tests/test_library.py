@@ -169,3 +169,44 @@ def test_swiglu_product_validation_errors(lib):
     # an expert's 2F weight rows must span < 2^30 bytes
     assert call(F=4096, ldhq=4096, ldgu=8192, ldhs=128, ldb=1 << 17, be=1 << 30) == 2
     assert call(F=0) == 0                               # no-op
+
+
+def test_fused_per_group_and_blockwise_validation_errors(lib):
+    P = 4096
+    # fp8_grouped_gemm_per_group_swiglu(a, sa, lda, b, sb, ldb, b_estride, offsets, E, M, F, K,
+    #                                   gu, ldgu, h, ldh, h_amax, stream)
+    f = lib.fp8_grouped_gemm_per_group_swiglu
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 64, 32, P, 128, P, 64, None, None) == 1  # amax
+    assert f(P, P, 32, P, P, 32, 4096, None, 4, 64, 64, 32, P, 128, P, 64, P, None) == 1
+    assert f(P, P, 32, P, P, 32, 4096, P, 0, 64, 64, 32, P, 128, P, 64, P, None) == 2     # E
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 40, 32, P, 128, P, 64, P, None) == 2     # F % 32
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 64, 32, P, 128, P, 48, P, None) == 2     # ldh < F
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 64, 32, P, 96, P, 64, P, None) == 2      # ldgu < 2F
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 64, 32, P, 128, P, 68, P, None) == 3     # ldh % 8
+    assert f(P, P, 32, P, P, 32, 4088, P, 4, 64, 64, 32, P, 128, P, 64, P, None) == 3     # b_estride
+    assert f(P, P, 32, P, P, 32, 4096, P, 4, 64, 64, 32, P, 128, None, 64, P, None) == 1  # h
+    # fp8_quantize_per_group_amax(x, M, K, ldx, offsets, E, amax, q, ldq, scales, ws, ws_bytes, s)
+    ws = lib.mxq_workspace_size(1, 0, 4, 0, 0)
+    assert ws == 16
+    g = lib.fp8_quantize_per_group_amax
+    assert g(P, 64, 32, 32, P, 4, None, P, 32, P, P, ws, None) == 1                     # amax
+    assert g(P, 64, 32, 32, P, 4, P, P, 32, P, P, ws - 4, None) == 5                    # ws
+    assert g(P, 64, 32, 36, P, 4, P, P, 32, P, P, ws, None) == 3                        # ldx % 8
+    gc = lib.fp8_quantize_per_group_colwise_amax
+    assert gc(P, 64, 32, 32, P, 4, None, P, 256, 256, P, P, P, ws, None) == 1
+    assert gc(P, 64, 32, 32, P, 4, P, P, 256, 250, P, P, P, ws, None) == 2              # M_cap
+    # blockwise: fp8_quantize_blockwise_act(x, M, K, ldx, q, ldq, scales, lds, s)
+    assert lib.fp8_quantize_blockwise_act(P, 8, 96, 96, P, 96, P, 1, None) == 2          # K % 128
+    assert lib.fp8_quantize_blockwise_act(P, 8, 128, 128, P, 128, P, 0, None) == 2       # lds
+    assert lib.fp8_quantize_blockwise_act(P, 8, 128, 132, P, 128, P, 1, None) == 3       # ldx % 8
+    assert lib.fp8_quantize_blockwise_act(None, 8, 128, 128, P, 128, P, 1, None) == 1
+    assert lib.fp8_quantize_blockwise_act(None, 0, 128, 128, None, 128, None, 1, None) == 0
+    assert lib.fp8_quantize_blockwise_weight(P, 200, 256, 256, P, 256, P, 1, None) == 2  # lds
+    assert lib.fp8_quantize_blockwise_weight(P + 8, 200, 256, 256, P, 256, P, 2, None) == 3
+    # fp8_gemm_blockwise(a, sa, lda, ldsa, b, sb, ldb, ldsb, M, N, K, c, ldc, out, accum, s)
+    h = lib.fp8_gemm_blockwise
+    assert h(P, P, 128, 1, P, P, 128, 1, 4, 4, 96, P, 4, 0, 0, None) == 2                # K % 128
+    assert h(P, P, 128, 0, P, P, 128, 1, 4, 4, 128, P, 4, 0, 0, None) == 2               # ldsa
+    assert h(P, None, 128, 1, P, P, 128, 1, 4, 4, 128, P, 4, 0, 0, None) == 1
+    assert h(P, P, 128, 1, P, P, 128, 1, 4, 4, 128, P, 4, 0, 3, None) == 4               # accum
+    assert h(P, P, 128, 1, P, P, 128, 1, 0, 4, 128, None, 4, 0, 0, None) == 0            # M = 0
