@@ -402,26 +402,21 @@ def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off
     every tensor quantized row-major and transposed each step, the six
     products on the per-group-scaled grouped GEMMs."""
     def step():
-        xq, xs = mxq.fp8_quantize_per_group(X, offs_d)
-        wq, ws = mxq.fp8_quantize_per_group(Wgu, w_off_gu)
+        # every tensor's row-major and transposed copies from one encoding pass
+        xq, xT, xs, poff = mxq.fp8_quantize_per_group_dual(X, offs_d)
+        wq, guT, ws, _ = mxq.fp8_quantize_per_group_dual(Wgu, w_off_gu)
         mxq.fp8_grouped_gemm_per_group(xq, xs, wq.view(E, 2 * FFN, HIDDEN), ws, offs_d)
-        hq, hs = mxq.fp8_quantize_per_group(h, offs_d)
-        dq, dsc = mxq.fp8_quantize_per_group(Wdn, w_off_dn)
+        hq, hT, hs, _ = mxq.fp8_quantize_per_group_dual(h, offs_d)
+        dq, dnT, dsc, _ = mxq.fp8_quantize_per_group_dual(Wdn, w_off_dn)
         mxq.fp8_grouped_gemm_per_group(hq, hs, dq.view(E, HIDDEN, FFN), dsc, offs_d)
-        gq, gs = mxq.fp8_quantize_per_group(dY, offs_d)
-        dnT, dnTs, _ = mxq.fp8_quantize_per_group_colwise(Wdn, w_off_dn)      # [1408, E*2048]
+        gq, dyT, gs, _ = mxq.fp8_quantize_per_group_dual(dY, offs_d)
         mxq.fp8_grouped_gemm_per_group(
-            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dnTs, offs_d)
-        uq, us = mxq.fp8_quantize_per_group(dGU, offs_d)
-        guT, guTs, _ = mxq.fp8_quantize_per_group_colwise(Wgu, w_off_gu)      # [2048, E*2816]
+            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dsc, offs_d)
+        uq, duT, us, _ = mxq.fp8_quantize_per_group_dual(dGU, offs_d)
         mxq.fp8_grouped_gemm_per_group(
-            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), guTs, offs_d)
-        dyT, dyTs, poff = mxq.fp8_quantize_per_group_colwise(dY, offs_d)
-        hT, hTs, _ = mxq.fp8_quantize_per_group_colwise(h, offs_d)
-        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, dyTs, hT, hTs, poff)
-        duT, duTs, _ = mxq.fp8_quantize_per_group_colwise(dGU, offs_d)
-        xT, xTs, _ = mxq.fp8_quantize_per_group_colwise(X, offs_d)
-        mxq.fp8_grouped_gemm_wgrad_per_group(duT, duTs, xT, xTs, poff)
+            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), ws, offs_d)
+        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, gs, hT, hs, poff)
+        mxq.fp8_grouped_gemm_wgrad_per_group(duT, us, xT, xs, poff)
 
     for _ in range(2):
         step()
@@ -435,7 +430,8 @@ def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
     return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
-            "quantization": "per-expert FP32 scales, row-major and transposed copies"}
+            "quantization": "per-expert FP32 scales, row-major and transposed copies from "
+                            "one encoding pass per tensor (fp8_quantize_per_group_dual)"}
 
 
 def graph_step(torch, step, flops, steps):

@@ -110,6 +110,36 @@ __device__ __forceinline__ float pt_div(float xv, float s, float r, bool direct)
   return __builtin_copysignf(__builtin_fmaf(rem, r, q0), xv);
 }
 
+// Codes of two BF16 values packed in w, for a tensor whose amax is NaN/Inf
+// (s == 1): NaN -> 0x7F|sign, +-Inf -> saturate.
+template <bool HI>
+__device__ __forceinline__ uint32_t pt_nonfinite_pair(uint32_t w, uint32_t old) {
+  uint32_t out = cvt2_e4m3_sat<HI>(bf16_lo(w), bf16_hi(w), old);
+  uint32_t sh = HI ? 16u : 0u;
+  uint32_t b0 = w & 0x7FFFu, b1 = (w >> 16) & 0x7FFFu;
+  if (b0 > 0x7F80u) out = (out & ~(0xFFu << sh)) | ((0x7Fu | ((w >> 8) & 0x80u)) << sh);
+  if (b1 > 0x7F80u) out = (out & ~(0xFFu << (sh + 8))) | ((0x7Fu | ((w >> 24) & 0x80u)) << (sh + 8));
+  return out;
+}
+
+// 8 BF16 values (one 16-byte load) -> 8 codes with scale s (r = RN(1/s)).
+__device__ __forceinline__ uint2 pt_encode8(uint4 v, float s, float r, bool direct,
+                                            bool nonfinite) {
+  uint32_t lo, hi;
+  if (nonfinite) {
+    lo = pt_nonfinite_pair<false>(v.x, 0u);
+    lo = pt_nonfinite_pair<true>(v.y, lo);
+    hi = pt_nonfinite_pair<false>(v.z, 0u);
+    hi = pt_nonfinite_pair<true>(v.w, hi);
+  } else {
+    lo = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.x), s, r, direct), pt_div(bf16_hi(v.x), s, r, direct), 0u);
+    lo = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.y), s, r, direct), pt_div(bf16_hi(v.y), s, r, direct), lo);
+    hi = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.z), s, r, direct), pt_div(bf16_hi(v.z), s, r, direct), 0u);
+    hi = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.w), s, r, direct), pt_div(bf16_hi(v.w), s, r, direct), hi);
+  }
+  return make_uint2(lo, hi);
+}
+
 // ---------------------------------------------------------------------------
 // Column-wise (grouped, zero-padded) MX quantization, transposed output.
 //
@@ -272,7 +302,19 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     for (int u = 0; u < 4; ++u)
       *reinterpret_cast<uint4*>(&tile[(u * 32 + (tid >> 3)) * kColLdsW + chunk * 4]) = cur[u];
     if (pass + 2 < kColPasses) load(kb + 2 * kColTileK, nx2);
-    if (ROW) {
+    if (ROW && PG) {
+      // Row-major copy with the group's FP32 scale (rows of block u belong to
+      // group s_grp[u]); the scales are the caller's group scales.
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = s_grp[u];
+        const float gs = e >= 0 ? gscale[e] : 1.0f;
+        const uint2 c = pt_encode8(cur[u], gs, __frcp_rn(gs), gs < 1.17549435e-38f,
+                                   e >= 0 && gmax[e] >= 0x7F80u);
+        const int64_t k = kb + chunk * 8;
+        if (rok[u] && k < K) store_stream(q + srow[u] * ldq + k, c);
+      }
+    } else if (ROW) {
       // Row-wise codes of the rows held in registers (every lane takes part
       // in the quad exchanges; only valid rows and columns are stored).
 #pragma unroll
@@ -430,18 +472,6 @@ __global__ __launch_bounds__(kPtThreads) void k_pt_amax(const uint16_t* __restri
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-// Codes of two BF16 values packed in w, for a tensor whose amax is NaN/Inf
-// (s == 1): NaN -> 0x7F|sign, +-Inf -> saturate.
-template <bool HI>
-__device__ __forceinline__ uint32_t pt_nonfinite_pair(uint32_t w, uint32_t old) {
-  uint32_t out = cvt2_e4m3_sat<HI>(bf16_lo(w), bf16_hi(w), old);
-  uint32_t sh = HI ? 16u : 0u;
-  uint32_t b0 = w & 0x7FFFu, b1 = (w >> 16) & 0x7FFFu;
-  if (b0 > 0x7F80u) out = (out & ~(0xFFu << sh)) | ((0x7Fu | ((w >> 8) & 0x80u)) << sh);
-  if (b1 > 0x7F80u) out = (out & ~(0xFFu << (sh + 8))) | ((0x7Fu | ((w >> 24) & 0x80u)) << (sh + 8));
-  return out;
-}
-
 __global__ __launch_bounds__(kPtThreads) void k_pt_quant(const uint16_t* __restrict__ x, int64_t n,
                                                          const uint32_t* __restrict__ partial, int nparts,
                                                          uint8_t* __restrict__ q, float* __restrict__ scale_out) {
@@ -493,24 +523,6 @@ __global__ __launch_bounds__(kPtThreads) void k_pt_quant(const uint16_t* __restr
 
 __device__ __forceinline__ float pt_block_scale(uint32_t m) {
   return (m < 0x7F80u && m != 0u) ? __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f) : 1.0f;
-}
-
-// 8 BF16 values (one 16-byte load) -> 8 codes with scale s (r = RN(1/s)).
-__device__ __forceinline__ uint2 pt_encode8(uint4 v, float s, float r, bool direct,
-                                            bool nonfinite) {
-  uint32_t lo, hi;
-  if (nonfinite) {
-    lo = pt_nonfinite_pair<false>(v.x, 0u);
-    lo = pt_nonfinite_pair<true>(v.y, lo);
-    hi = pt_nonfinite_pair<false>(v.z, 0u);
-    hi = pt_nonfinite_pair<true>(v.w, hi);
-  } else {
-    lo = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.x), s, r, direct), pt_div(bf16_hi(v.x), s, r, direct), 0u);
-    lo = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.y), s, r, direct), pt_div(bf16_hi(v.y), s, r, direct), lo);
-    hi = cvt2_e4m3_sat<false>(pt_div(bf16_lo(v.z), s, r, direct), pt_div(bf16_hi(v.z), s, r, direct), 0u);
-    hi = cvt2_e4m3_sat<true>(pt_div(bf16_lo(v.w), s, r, direct), pt_div(bf16_hi(v.w), s, r, direct), hi);
-  }
-  return make_uint2(lo, hi);
 }
 
 constexpr int kDppRowMirror = 0x140;       // lane i <- lane 15 - i within a row of 16
@@ -958,6 +970,43 @@ extern "C" int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M,
   if (!amax) return MXQ_ERR_NULL;
   return quantize_per_group_colwise(x, M, K, ldx, offsets, E, amax, qT, ldqT, M_cap, scales,
                                     offsets_padded, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t K,
+                                           int64_t ldx, const int64_t* offsets, int32_t E,
+                                           uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                                           int64_t M_cap, float* scales,
+                                           int64_t* offsets_padded, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (E < 1 || E > kPgMaxGroups || E > kColMaxGroupsLds) return MXQ_ERR_SHAPE;
+  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
+  if (K % 8 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  if (K > 0 && M_cap > 0) {
+    if (!qT || (M > 0 && (!x || !q))) return MXQ_ERR_NULL;
+    if (ldqT < M_cap || (M > 0 && (ldx < K || ldq < K))) return MXQ_ERR_SHAPE;
+    if (ldqT % 16 != 0 || !aligned(qT, 16) ||
+        (M > 0 && (ldx % 8 != 0 || !aligned(x, 16) || ldq % 8 != 0 || !aligned(q, 8))))
+      return MXQ_ERR_ALIGN;
+  }
+  if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
+    return MXQ_ERR_WORKSPACE;
+  uint32_t* rowmax = static_cast<uint32_t*>(workspace);
+  uint32_t* gmax = rowmax + M;
+  const int64_t waves = (int64_t)num_cus() * 64;
+  const int64_t rows_blocks = (M + 3) / 4;
+  const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
+                                                             : waves / 4);
+  int st = pg_scales(x, M, K, ldx, offsets, E, nullptr, rowmax, gmax, scales, blocks, stream);
+  if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
+  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
+  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  hipLaunchKernelGGL((k_mx_colwise<true, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
+                     x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded, q, ldq,
+                     nullptr, 0, gmax, scales);
+  return launch_status();
 }
 
 extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,

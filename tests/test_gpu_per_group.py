@@ -345,3 +345,65 @@ def test_per_group_dgrad_with_transposed_weights():
                 float(sgh[e]) * float(swh[e])
     T = T + 2.0 ** -23 * np.abs(Y)
     assert gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T).all()
+
+
+# ---------------------------------------------------------------------------
+# both copies in one pass
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("counts,K", [
+    ([40, 0, 1, 130, 0, 300, 0], 64),
+    ([1000, 17, 0, 2, 511], 2048),
+    ([5], 8),
+    ([0, 0, 257], 136),
+])
+def test_per_group_dual_bit_exact(counts, K):
+    say(f"per-group dual quant counts={counts} K={K}")
+    offs = workloads.offsets_from_counts(np.array(counts, np.int64))
+    M = int(offs[-1])
+    x = workloads.bf16_normal((M, K), 1.0, seed=M + 3 * K, name="pgd", outlier_frac=0.01,
+                              outlier_scale=40.0)
+    q, qT, s, poff = mxq.fp8_quantize_per_group_dual(to_dev_bf16(x), to_dev(offs))
+    rq, rs = per_tensor.pg_quantize(x, offs)
+    cq, cs, cp = per_tensor.pg_quantize_colwise(x, offs)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(cs.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(poff), cp)
+    assert np.array_equal(host(qT)[:, :int(cp[-1])], cq)
+
+
+def test_per_group_dual_special_groups():
+    """NaN, Inf, zero and empty groups, as the oracle."""
+    K = 64
+    offs = np.array([0, 3, 3, 40, 41, 90], np.int64)
+    vals = np.random.default_rng(8).normal(0, 1, (90, K))
+    vals[1, 5] = np.nan
+    vals[20, 0] = np.inf
+    vals[40] = 0.0
+    bits = codec.bf16_round_to_bits(vals)
+    q, qT, s, poff = mxq.fp8_quantize_per_group_dual(to_dev_bf16(bits), to_dev(offs))
+    rq, rs = per_tensor.pg_quantize(bits, offs)
+    cq, _, cp = per_tensor.pg_quantize_colwise(bits, offs)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(qT)[:, :int(cp[-1])], cq)
+
+
+def test_per_group_dual_equals_single_copies_full_size():
+    """dGU [49152, 2816] over the 64 expert groups, and W_gu [64 x 2816, 2048]
+    with one group per expert: byte-equal to the row-major and transposed
+    single-copy quantizers (each pinned to the oracle above)."""
+    say("per-group dual quant, full-size dGU and W_gu")
+    bw = workloads.moe_backward(0)
+    fw = workloads.moe_forward(0)
+    cases = [(bw["dGU"], fw["offsets"]),
+             (fw["W_gu"].reshape(64 * 2816, 2048), np.arange(65, dtype=np.int64) * 2816)]
+    for bits, offs in cases:
+        xd, od = to_dev_bf16(bits), to_dev(offs)
+        q, qT, s, poff = mxq.fp8_quantize_per_group_dual(xd, od)
+        q1, s1 = mxq.fp8_quantize_per_group(xd, od)
+        qT2, s2, p2 = mxq.fp8_quantize_per_group_colwise(xd, od)
+        Mp = int(host(p2)[-1])
+        assert torch.equal(q, q1) and torch.equal(s, s1) and torch.equal(s, s2)
+        assert torch.equal(poff, p2) and torch.equal(qT[:, :Mp], qT2[:, :Mp])
