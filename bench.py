@@ -528,28 +528,22 @@ def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn,
     _, t_pg_qt = _timed(torch, mxq.fp8_quantize_per_group_colwise, ph, offs_d)
     def pg_step():
         # the per-expert-scaling step with the fused producer: h's group amaxes
-        # come from the gate/up epilogue
-        xq, xs = mxq.fp8_quantize_per_group(X, offs_d)
-        wq, ws = mxq.fp8_quantize_per_group(Wgu, w_off_gu)
+        # come from the gate/up epilogue (h's dual quantization has no amax pass)
+        xq, xT, xs, poff = mxq.fp8_quantize_per_group_dual(X, offs_d)
+        wq, guT, ws, _ = mxq.fp8_quantize_per_group_dual(Wgu, w_off_gu)
         _, hb, ham = mxq.fp8_grouped_gemm_per_group_swiglu(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
                                                           ws, offs_d)
-        hq, hs = mxq.fp8_quantize_per_group_amax(hb, offs_d, ham)
-        dq, dsc = mxq.fp8_quantize_per_group(Wdn, w_off_dn)
+        hq, hT, hs, _ = mxq.fp8_quantize_per_group_dual(hb, offs_d, amax=ham)
+        dq, dnT, dsc, _ = mxq.fp8_quantize_per_group_dual(Wdn, w_off_dn)
         mxq.fp8_grouped_gemm_per_group(hq, hs, dq.view(E, HIDDEN, FFN), dsc, offs_d)
-        gq, gs = mxq.fp8_quantize_per_group(dY, offs_d)
-        dnT, dnTs, _ = mxq.fp8_quantize_per_group_colwise(Wdn, w_off_dn)
+        gq, dyT, gs, _ = mxq.fp8_quantize_per_group_dual(dY, offs_d)
         mxq.fp8_grouped_gemm_per_group(
-            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dnTs, offs_d)
-        uq, us = mxq.fp8_quantize_per_group(dGU, offs_d)
-        guT, guTs, _ = mxq.fp8_quantize_per_group_colwise(Wgu, w_off_gu)
+            gq, gs, dnT[:, :E * HIDDEN].view(FFN, E, HIDDEN).permute(1, 0, 2), dsc, offs_d)
+        uq, duT, us, _ = mxq.fp8_quantize_per_group_dual(dGU, offs_d)
         mxq.fp8_grouped_gemm_per_group(
-            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), guTs, offs_d)
-        dyT, dyTs, poff = mxq.fp8_quantize_per_group_colwise(dY, offs_d)
-        hT, hTs, _ = mxq.fp8_quantize_per_group_colwise_amax(hb, offs_d, ham)
-        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, dyTs, hT, hTs, poff)
-        duT, duTs, _ = mxq.fp8_quantize_per_group_colwise(dGU, offs_d)
-        xT, xTs, _ = mxq.fp8_quantize_per_group_colwise(X, offs_d)
-        mxq.fp8_grouped_gemm_wgrad_per_group(duT, duTs, xT, xTs, poff)
+            uq, us, guT[:, :E * 2 * FFN].view(HIDDEN, E, 2 * FFN).permute(1, 0, 2), ws, offs_d)
+        mxq.fp8_grouped_gemm_wgrad_per_group(dyT, gs, hT, hs, poff)
+        mxq.fp8_grouped_gemm_wgrad_per_group(duT, us, xT, xs, poff)
 
     _, t_pg_step = _timed(torch, pg_step)
     pg = {

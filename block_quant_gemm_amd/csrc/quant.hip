@@ -974,6 +974,7 @@ extern "C" int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M,
 
 extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t K,
                                            int64_t ldx, const int64_t* offsets, int32_t E,
+                                           const float* amax,
                                            uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                                            int64_t M_cap, float* scales,
                                            int64_t* offsets_padded, void* workspace,
@@ -990,15 +991,16 @@ extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t
       return MXQ_ERR_ALIGN;
   }
   if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
-  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0))
+  const int64_t ws_rows = amax ? 0 : M;              // row maxima only without amaxes
+  if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, ws_rows, E, 0, 0))
     return MXQ_ERR_WORKSPACE;
   uint32_t* rowmax = static_cast<uint32_t*>(workspace);
-  uint32_t* gmax = rowmax + M;
+  uint32_t* gmax = rowmax + ws_rows;
   const int64_t waves = (int64_t)num_cus() * 64;
   const int64_t rows_blocks = (M + 3) / 4;
   const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
                                                              : waves / 4);
-  int st = pg_scales(x, M, K, ldx, offsets, E, nullptr, rowmax, gmax, scales, blocks, stream);
+  int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
   const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
   const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);

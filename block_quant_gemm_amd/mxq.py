@@ -56,8 +56,8 @@ _SIGS = {
                                                      _p]),
     "fp8_gemm_blockwise": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64,
                                           _i64, _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
-    "fp8_quantize_per_group_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p,
-                                                   _i64, _i64, _p, _p, _p, _sz, _p]),
+    "fp8_quantize_per_group_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _p, _i64,
+                                                   _p, _i64, _i64, _p, _p, _p, _sz, _p]),
     "fp8_quantize_per_group_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64,
                                                       _i64, _p, _p, _p, _sz, _p]),
     "fp8_grouped_gemm_wgrad_per_group": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _p, _i32,
@@ -274,10 +274,12 @@ def fp8_quantize_per_group_colwise(x, offsets, M_cap=None, qT=None, scales=None,
     return qT, scales, offsets_padded
 
 
-def fp8_quantize_per_group_dual(x, offsets, M_cap=None, q=None, qT=None, scales=None,
+def fp8_quantize_per_group_dual(x, offsets, amax=None, M_cap=None, q=None, qT=None, scales=None,
                                 offsets_padded=None, workspace=None):
-    """Both per-group copies in one encoding pass.  Returns (codes uint8 [M, K],
-    codesT uint8 [K, M_cap], scales float32 [E], offsets_padded int64 [E+1])."""
+    """Both per-group copies in one encoding pass (``amax``: the groups'
+    amaxes, float32 [E], to skip the amax pass).  Returns (codes uint8
+    [M, K], codesT uint8 [K, M_cap], scales float32 [E], offsets_padded
+    int64 [E+1])."""
     x = _bf16_bits(x)
     M, K = x.shape
     E = offsets.numel() - 1
@@ -292,10 +294,10 @@ def fp8_quantize_per_group_dual(x, offsets, M_cap=None, q=None, qT=None, scales=
     if offsets_padded is None:
         offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
     if workspace is None:
-        workspace = torch.empty(max(workspace_size(WS_PER_GROUP, M, E), 4), dtype=torch.uint8,
-                                device=x.device)
+        workspace = torch.empty(max(workspace_size(WS_PER_GROUP, 0 if amax is not None else M, E),
+                                    4), dtype=torch.uint8, device=x.device)
     _check(load().fp8_quantize_per_group_dual(
-        _ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q), q.stride(0), _ptr(qT),
+        _ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(amax), _ptr(q), q.stride(0), _ptr(qT),
         qT.stride(0), M_cap, _ptr(scales), _ptr(offsets_padded), _ptr(workspace),
         workspace.numel(), _stream()))
     return q, qT, scales, offsets_padded

@@ -233,6 +233,10 @@ MXQ_API int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M, in
  * mx_quantize_dual): the row-major codes of fp8_quantize_per_group and the
  * transposed, group-padded codes of fp8_quantize_per_group_colwise, with the
  * same group scales, after one amax pass over x.
+ *   amax     : device float[E] of the groups' amaxes, as for
+ *              fp8_quantize_per_group_amax (then there is no amax pass and the
+ *              workspace needs mxq_workspace_size(MXQ_WS_PER_GROUP, 0, E, 0, 0)
+ *              bytes), or NULL.
  *   q, ldq   : device E4M3 [M, K] (ldq % 8 == 0, 8-byte aligned).
  *   qT, ldqT, M_cap, scales, offsets_padded : as fp8_quantize_per_group_colwise.
  *   workspace: mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0) bytes.
@@ -240,7 +244,7 @@ MXQ_API int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M, in
  * M + 31*E holds every group's padding).
  */
 MXQ_API int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                const int64_t* offsets, int32_t E,
+                                const int64_t* offsets, int32_t E, const float* amax,
                                 uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
                                 int64_t M_cap, float* scales, int64_t* offsets_padded,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -62,8 +62,10 @@ def _fused_and_per_group(d):
     _, ph, pam = mxq.fp8_grouped_gemm_per_group_swiglu(pxq, pxs, pwq.view(E, 2 * F, H), pws, o)
     q1, s1 = mxq.fp8_quantize_per_group_amax(ph, o, pam)
     t1, ts1, _ = mxq.fp8_quantize_per_group_colwise_amax(ph, o, pam)
+    dq, dT, ds, _ = mxq.fp8_quantize_per_group_dual(ph, o, amax=pam)
     Mp = d["Mp"]
-    return [gu, hq, hs, hqT[:, :Mp], hsT[:, :Mp // 32], poff, ph, pam, q1, s1, t1[:, :Mp], ts1]
+    return [gu, hq, hs, hqT[:, :Mp], hsT[:, :Mp // 32], poff, ph, pam, q1, s1, t1[:, :Mp], ts1,
+            dq, dT[:, :Mp], ds]
 
 
 def _bits(ts):

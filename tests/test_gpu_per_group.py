@@ -407,3 +407,20 @@ def test_per_group_dual_equals_single_copies_full_size():
         Mp = int(host(p2)[-1])
         assert torch.equal(q, q1) and torch.equal(s, s1) and torch.equal(s, s2)
         assert torch.equal(poff, p2) and torch.equal(qT[:, :Mp], qT2[:, :Mp])
+
+
+def test_per_group_dual_with_given_amax():
+    """With the groups' amaxes given, the same codes and scales as the oracle."""
+    offs = workloads.offsets_from_counts(np.array([300, 0, 1, 77], np.int64))
+    x = workloads.bf16_normal((378, 256), 1.0, seed=4, name="pgda", outlier_frac=0.02,
+                              outlier_scale=20.0)
+    xv = codec.bf16_bits_to_f64(x)
+    amax = np.array([np.abs(xv[offs[e]:offs[e + 1]]).max() if offs[e + 1] > offs[e] else 0.0
+                     for e in range(4)], np.float32)
+    q, qT, s, poff = mxq.fp8_quantize_per_group_dual(to_dev_bf16(x), to_dev(offs),
+                                                     amax=to_dev(amax))
+    rq, rs = per_tensor.pg_quantize(x, offs)
+    cq, _, cp = per_tensor.pg_quantize_colwise(x, offs)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(qT)[:, :int(cp[-1])], cq)

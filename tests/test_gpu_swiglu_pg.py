@@ -130,6 +130,13 @@ def test_per_group_swiglu_product(counts, F, K):
     t2 = mxq.fp8_quantize_per_group_colwise(h, offs_d)
     for x1, x2 in zip(t1, t2):
         assert np.array_equal(host(x1), host(x2))
+    d1 = mxq.fp8_quantize_per_group_dual(h, offs_d, amax=h_amax)
+    d2 = mxq.fp8_quantize_per_group_dual(h, offs_d)
+    Mp = int(host(d2[3])[-1])
+    assert np.array_equal(host(d1[0]), host(d2[0]))
+    assert np.array_equal(host(d1[1])[:, :Mp], host(d2[1])[:, :Mp])
+    assert np.array_equal(host(d1[2]).view(np.uint32), host(d2[2]).view(np.uint32))
+    assert np.array_equal(host(d1[3]), host(d2[3]))
 
 
 def test_per_group_swiglu_full_size_sampled():

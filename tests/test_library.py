@@ -195,6 +195,13 @@ def test_fused_per_group_and_blockwise_validation_errors(lib):
     gc = lib.fp8_quantize_per_group_colwise_amax
     assert gc(P, 64, 32, 32, P, 4, None, P, 256, 256, P, P, P, ws, None) == 1
     assert gc(P, 64, 32, 32, P, 4, P, P, 256, 250, P, P, P, ws, None) == 2              # M_cap
+    # fp8_quantize_per_group_dual(x, M, K, ldx, offsets, E, amax, q, ldq, qT, ldqT, M_cap,
+    #                             scales, offsets_padded, ws, ws_bytes, s)
+    d = lib.fp8_quantize_per_group_dual
+    assert d(P, 64, 32, 32, P, 4, None, P, 32, P, 256, 256, P, P, P, ws, None) == 5    # row maxima
+    assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 256, P, P, P, ws - 4, None) == 5   # amax given
+    assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 250, P, P, P, ws, None) == 2       # M_cap
+    assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 256, None, P, P, ws, None) == 1    # scales
     # blockwise: fp8_quantize_blockwise_act(x, M, K, ldx, q, ldq, scales, lds, s)
     assert lib.fp8_quantize_blockwise_act(P, 8, 96, 96, P, 96, P, 1, None) == 2          # K % 128
     assert lib.fp8_quantize_blockwise_act(P, 8, 128, 128, P, 128, P, 0, None) == 2       # lds
