@@ -58,6 +58,8 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense FFN component")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the full block step (16384 tokens) component")
     ap.add_argument("--step-only", action="store_true",
                     help="only the expert-layer step (no dense, per-expert, fused or BF16 "
                          "components), e.g. for counter passes")
@@ -78,9 +80,14 @@ class Timer:
         self.torch = torch
         self.ev = {}
         self.on = False
+        self.only = None                         # record this label alone (None: all)
+
+    def reset(self, only=None):
+        self.ev = {}
+        self.only = only
 
     def run(self, label, fn, *a, **k):
-        if not self.on:
+        if not self.on or (self.only is not None and label != self.only):
             return fn(*a, **k)
         s = self.torch.cuda.Event(enable_timing=True)
         e = self.torch.cuda.Event(enable_timing=True)
@@ -194,6 +201,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Breakdown pass (K steps, not the timed region): HIP events around every
+    # launch give each kernel class's share of the step.  Each recorded event
+    # costs the stream a few microseconds, so the timed region below records
+    # events around the roofline kernel's launches only.
+    T.on = True
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    T.on = False
+    avg_ms = T.ms()
+    n_launch = T.count()
+    per_step_ms = {k: avg_ms[k] * n_launch[k] / args.steps for k in avg_ms}
+    dom = max(per_step_ms, key=per_step_ms.get)
+
+    T.reset(only=dom)
     T.on = True
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -203,6 +225,7 @@ def main():
     t1 = time.perf_counter()
     T.on = False
     ms_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = T.ms()[dom]                          # the roofline kernel, timed region
 
     # ---------------- algorithmic work ----------------
     per_dir = 2 * M * (2 * FFN * HIDDEN + HIDDEN * FFN)       # fwd (= dgrad = wgrad) FLOPs
@@ -218,15 +241,12 @@ def main():
     }
     quant_bpe = {"q_row": MX_BYTES_PER_ELT, "q_col": MX_BYTES_PER_ELT,
                  "q_dual": DUAL_BYTES_PER_ELT}
-    qkeys = [k for k in ("q_row", "q_col", "q_dual") if k in avg_ms_keys(T)]
+    qkeys = [k for k in ("q_row", "q_col", "q_dual") if k in avg_ms]
     gemm_flops = {
         "gmm": [2 * M * 2 * FFN * HIDDEN, 2 * M * HIDDEN * FFN, 2 * M * FFN * HIDDEN,
                 2 * M * HIDDEN * 2 * FFN],
         "wgrad": [2 * M * HIDDEN * FFN, 2 * M * 2 * FFN * HIDDEN],
     }
-    avg_ms = T.ms()
-    n_launch = T.count()
-    per_step_ms = {k: avg_ms[k] * n_launch[k] / args.steps for k in avg_ms}
     breakdown = {}
     for k in qkeys:
         work = sum(quant_elts[k]) * quant_bpe[k]
@@ -246,16 +266,17 @@ def main():
     quant_ms = sum(per_step_ms[k] for k in qkeys)
     quant_bytes = sum(sum(quant_elts[k]) * quant_bpe[k] for k in qkeys)
 
-    dom = max(per_step_ms, key=per_step_ms.get)
     if dom in gemm_flops:
         per_launch = sum(gemm_flops[dom]) / len(gemm_flops[dom])
-        achieved = per_launch / (avg_ms[dom] * 1e-3) / 1e12
-        roof = {"kernel": KFN[dom], "bound": "mfma", "achieved": achieved,
+        achieved = per_launch / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": KFN[dom], "avg_launch_us": dom_ms * 1e3, "bound": "mfma",
+                "achieved": achieved,
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS}
     else:
         per_launch = sum(quant_elts[dom]) * quant_bpe[dom] / len(quant_elts[dom])
-        achieved = per_launch / (avg_ms[dom] * 1e-3) / 1e9
-        roof = {"kernel": KFN[dom], "bound": "hbm", "achieved": achieved,
+        achieved = per_launch / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": KFN[dom], "avg_launch_us": dom_ms * 1e3, "bound": "hbm",
+                "achieved": achieved,
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS}
     roof["traffic"] = measured_traffic(roof["kernel"])
 
@@ -264,7 +285,10 @@ def main():
                   "quant_only_GB_per_s": quant_bytes / (quant_ms * 1e-3) / 1e9,
                   "gemm_ms_per_step": gemm_ms, "quant_ms_per_step": quant_ms}
     if not args.step_only:
+        components["step_distribution"] = step_distribution(torch, step, flops)
         components["step_as_hip_graph"] = graph_step(torch, step, flops, args.steps)
+        components["weights_quantized_once"] = weights_once_step(
+            torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
     if not args.no_dense and not args.step_only:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
     if not args.step_only:
@@ -272,6 +296,8 @@ def main():
             torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
         components["fused_swiglu_producer"] = fused_producer(
             torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
+    if not args.no_block and not args.step_only:
+        components["full_block_step"] = full_block_step(torch, mxq, workloads, args.seed)
     if not args.no_bf16_sweep and not args.step_only:
         components["bf16_vs_mx_forward_sweep"] = bf16_sweep(torch, mxq)
         components["bf16_moe_step"] = bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts,
@@ -300,10 +326,6 @@ def main():
         "components": components,
     }
     print(json.dumps(line), flush=True)
-
-
-def avg_ms_keys(T):
-    return set(T.ev)
 
 
 def measured_traffic(kernel):
@@ -569,6 +591,129 @@ def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn,
             "note": "h is the SwiGLU of the gate/up product; no separate h input or its "
                     "quantization"},
     }
+
+
+def step_distribution(torch, step, flops, n=50):
+    """Per-step times of the same step over n steps, each between HIP events
+    on the launch stream (after the timed region, so the clocks are warm):
+    median and 10th / 90th percentiles."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for s, e in ev:
+        s.record()
+        step()
+        e.record()
+    torch.cuda.synchronize()
+    import numpy as np
+    t = np.array([s.elapsed_time(e) for s, e in ev])
+    med = float(np.median(t))
+    return {"steps": n, "median_ms": med, "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)),
+            "TFLOP_per_s_at_median": flops / (med * 1e-3) / 1e12}
+
+
+def weights_once_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops):
+    """The expert-layer step with the weights' row and column copies made once
+    (weights change once per optimizer step, so their quantization is shared
+    by every micro-batch of it); activations and gradients still quantized in
+    the step."""
+    wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(Wgu, w_off_gu)
+    dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(Wdn, w_off_dn)
+    bq, bs = mxq.expert_view(dnT, dnTs, E, HIDDEN)
+    bq2, bs2 = mxq.expert_view(guT, guTs, E, 2 * FFN)
+
+    def step():
+        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(X, offs_d)
+        mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                            ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
+        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(h, offs_d)
+        mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
+                            offs_d)
+        gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(dY, offs_d)
+        mxq.mx_grouped_gemm(gq, gs, bq, bs, offs_d)
+        uq, us, duT, duTs, _ = mxq.mx_quantize_dual(dGU, offs_d)
+        mxq.mx_grouped_gemm(uq, us, bq2, bs2, offs_d)
+        mxq.mx_grouped_gemm_wgrad(dyT, dyTs, hT, hTs, poff)
+        mxq.mx_grouped_gemm_wgrad(duT, duTs, xT, xTs, poff)
+
+    _, ms = _timed(torch, step, reps=10)
+    return {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
+            "note": "W_gu and W_dn dual-quantized once outside the step"}
+
+
+def full_block_step(torch, mxq, workloads, seed):
+    """One block at sequence 4096 x batch 4 (16384 tokens): the MLA projection
+    and shared-expert Linears and the 64-expert routed products at 98304 rows,
+    forward, dgrad and wgrad, every operand MX-quantized in both directions by
+    the dual-axis quantizer in the step; and the same with the weights'
+    copies made once.  Tensors are drawn on the device with torch's generator
+    (N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients); expert
+    counts as for the expert layer, from 98304 rows."""
+    dev = torch.device("cuda:0")
+    T = workloads.BLOCK_TOKENS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def draw(shape, sigma):
+        return (torch.randn(shape, device=dev, generator=gen) * sigma).to(torch.bfloat16)
+
+    one = torch.tensor([0, T], dtype=torch.int64, device=dev)
+    dense = []
+    for name, fin, fout in workloads.BLOCK_DENSE_LINEARS:
+        dense.append(dict(X=draw((T, fin), 1.0), W=draw((fout, fin), 0.02),
+                          dY=draw((T, fout), 1e-3), fin=fin, fout=fout,
+                          woff=torch.tensor([0, fout], dtype=torch.int64, device=dev)))
+    counts = workloads.moe_counts(seed, T)
+    M = int(counts.sum())
+    offs_d = torch.from_numpy(workloads.offsets_from_counts(counts)).to(dev)
+    rX, rh = draw((M, HIDDEN), 1.0), draw((M, FFN), 1.0)
+    rdY, rdGU = draw((M, HIDDEN), 1e-3), draw((M, 2 * FFN), 1e-3)
+    Wgu, Wdn = draw((E * 2 * FFN, HIDDEN), 0.02), draw((E * HIDDEN, FFN), 0.02)
+    w_off_gu = torch.arange(E + 1, dtype=torch.int64, device=dev) * (2 * FFN)
+    w_off_dn = torch.arange(E + 1, dtype=torch.int64, device=dev) * HIDDEN
+
+    def quant_weights():
+        qw = [mxq.mx_quantize_dual(d["W"], d["woff"]) for d in dense]
+        return qw, mxq.mx_quantize_dual(Wgu, w_off_gu), mxq.mx_quantize_dual(Wdn, w_off_dn)
+
+    def step(wts=None):
+        qw, qgu, qdn = wts if wts is not None else quant_weights()
+        for d, (wq, ws, wT, wTs, _) in zip(dense, qw):
+            fout = d["fout"]
+            xq, xs, xT, xTs, _ = mxq.mx_quantize_dual(d["X"], one)
+            gq, gs, gT, gTs, _ = mxq.mx_quantize_dual(d["dY"], one)
+            mxq.mx_gemm(xq, xs, wq, ws)                                    # Y = X Wᵀ
+            mxq.mx_gemm(gq, gs, wT[:, :fout], wTs[:, :fout // 32])         # dX = dY W
+            mxq.mx_gemm(gT[:, :T], gTs[:, :T // 32], xT[:, :T], xTs[:, :T // 32])  # dW
+        wq, ws, guT, guTs, _ = qgu
+        dq, dsc, dnT, dnTs, _ = qdn
+        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(rX, offs_d)
+        mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                            ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
+        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(rh, offs_d)
+        mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
+                            offs_d)
+        gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(rdY, offs_d)
+        bq, bs = mxq.expert_view(dnT, dnTs, E, HIDDEN)
+        mxq.mx_grouped_gemm(gq, gs, bq, bs, offs_d)
+        uq, us, duT, duTs, _ = mxq.mx_quantize_dual(rdGU, offs_d)
+        bq2, bs2 = mxq.expert_view(guT, guTs, E, 2 * FFN)
+        mxq.mx_grouped_gemm(uq, us, bq2, bs2, offs_d)
+        mxq.mx_grouped_gemm_wgrad(dyT, dyTs, hT, hTs, poff)
+        mxq.mx_grouped_gemm_wgrad(duT, duTs, xT, xTs, poff)
+
+    dense_flops = sum(6 * T * fin * fout for _, fin, fout in workloads.BLOCK_DENSE_LINEARS)
+    moe_flops = 6 * M * (2 * FFN * HIDDEN + HIDDEN * FFN)
+    flops = dense_flops + moe_flops
+    _, ms = _timed(torch, step, reps=5)
+    wts = quant_weights()
+    _, ms_once = _timed(torch, step, wts, reps=5)
+    return {"tokens": T, "routed_rows": M, "algorithmic_flops": flops,
+            "dense_flops": dense_flops, "routed_flops": moe_flops,
+            "ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
+            "weights_quantized_once": {"ms_per_step": ms_once,
+                                       "TFLOP_per_s_incl_quant": flops / (ms_once * 1e-3) / 1e12},
+            "data": "device-drawn synthetic tensors (torch generator, seeded)"}
 
 
 def bf16_sweep(torch, mxq, reps=10):
