@@ -797,23 +797,31 @@ def bf16_moe_step(torch, X, h, Wgu, Wdn, dY, dGU, counts, mx_ms, reps=5):
 def cpu_baseline(fw, bw, budget_s):
     """The CPU oracle (unchanged) on a bounded sample of the same step: whole
     experts, smallest first, until about ``budget_s`` seconds of CPU time;
-    TFLOP/s = the sample's algorithmic GEMM FLOPs / oracle time."""
+    TFLOP/s = the sample's algorithmic GEMM FLOPs / oracle time.  The
+    smallest expert is also timed with the BLAS pool limited to one thread."""
     import numpy as np
     from oracle import gemm, mx
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max((i.get("num_threads", 1) for i in threadpool_info()
                        if i.get("user_api") == "blas"), default=1)
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
 
     counts, offs = fw["counts"], fw["offsets"]
-    order = np.argsort(counts, kind="stable")
-    done, flops, t_tot = [], 0, 0.0
-    for e in order:
+
+    def expert(e):
+        """The oracle's forward, dgrad and wgrad of expert e; its GEMM FLOPs."""
         lo, hi = int(offs[e]), int(offs[e + 1])
-        t0 = time.perf_counter()
         xq, xs = mx.mx_quantize_rowwise(fw["X"][lo:hi])
         wq, ws = mx.mx_quantize_rowwise(fw["W_gu"][e])
         gemm.gemm_ref(mx.mx_dequantize(xq, xs), mx.mx_dequantize(wq, ws))
@@ -833,17 +841,32 @@ def cpu_baseline(fw, bw, budget_s):
         aT, aTs, p = mx.mx_quantize_grouped_colwise(bw["dGU"][lo:hi], one)
         bT, bTs, _ = mx.mx_quantize_grouped_colwise(fw["X"][lo:hi], one)
         gemm.grouped_wgrad_ref(mx.mx_dequantize(aT, aTs), mx.mx_dequantize(bT, bTs), p)
+        return 6 * (hi - lo) * (2 * FFN * HIDDEN + HIDDEN * FFN)
+
+    order = np.argsort(counts, kind="stable")
+    done, flops, t_tot = [], 0, 0.0
+    for e in order:
+        t0 = time.perf_counter()
+        flops += expert(e)
         t_tot += time.perf_counter() - t0
-        flops += 6 * (hi - lo) * (2 * FFN * HIDDEN + HIDDEN * FFN)
         done.append(int(e))
         if t_tot >= budget_s:
             break
+    single = None
+    if threadpool_limits is not None and len(order):
+        with threadpool_limits(limits=1, user_api="blas"):
+            t0 = time.perf_counter()
+            f1 = expert(order[0])
+            t1 = time.perf_counter() - t0
+        single = {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                  "sample": "the smallest expert (%d rows), %.1f s" % (int(counts[order[0]]), t1)}
     return {"value": flops / t_tot / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "host_cpus": os.cpu_count(),
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model, "blas_threads": int(threads),
             "sample": "full fwd+dgrad+wgrad oracle path (quant, dequant, FP64 GEMM and "
                       "|A|·|B| magnitudes) for %d whole experts, smallest first (%d rows); "
-                      "%.1f s" % (len(done), sum(int(counts[e]) for e in done), t_tot)}
+                      "%.1f s" % (len(done), sum(int(counts[e]) for e in done), t_tot),
+            "single_thread": single}
 
 
 if __name__ == "__main__":
