@@ -60,12 +60,6 @@ def offsets_from_counts(counts):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
 
 
-def padded_counts(counts, multiple=32):
-    """Group sizes rounded up to a multiple of ``multiple`` (wgrad padding)."""
-    counts = np.asarray(counts, dtype=np.int64)
-    return (counts + multiple - 1) // multiple * multiple
-
-
 # --- named workloads -------------------------------------------------------
 
 def tiny_linear(seed=0):

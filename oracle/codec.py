@@ -94,11 +94,6 @@ def bf16_bits_to_f64(bits):
         return b.view(np.float32).astype(np.float64)
 
 
-def f64_to_f32_bits(values):
-    """float64 -> FP32 bit patterns (uint32), IEEE round to nearest even."""
-    return np.asarray(values, dtype=np.float64).astype(np.float32).view(np.uint32)
-
-
 def bf16_round(values):
     """Round float64 values to the nearest BF16 value, ties to even, as float64.
 

@@ -5,7 +5,6 @@ check itself.  CPU only."""
 from fractions import Fraction
 
 import numpy as np
-import pytest
 
 from oracle import codec, gemm, mx, per_tensor
 from block_quant_gemm_amd import workloads
