@@ -392,6 +392,45 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
                       (cv.float() - ours.float()).abs().max() / cv.float().abs().max()).item()}
     except (RuntimeError, AttributeError) as ex:        # not built into this torch
         vendor = {"unavailable": str(ex).splitlines()[0][:200]}
+    # Each format's whole path (both quantizations and the GEMM) from cold caches:
+    # a 1 GiB write before every call evicts the 256 MB last-level cache, which
+    # would otherwise hold these inputs (X 34 MB, W 45 MB) between calls.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=X.device)
+
+    def cold(path):
+        ts = []
+        for i in range(reps + 1):
+            flush.fill_(i & 0xFF)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            path()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    def mx_path():
+        a, sa = mxq.mx_quantize_rowwise(X)
+        b, sb = mxq.mx_quantize_rowwise(W)
+        mxq.mx_gemm(a, sa, b, sb)
+
+    def pt_path():
+        a, sa = mxq.fp8_quantize_per_tensor(X)
+        b, sb = mxq.fp8_quantize_per_tensor(W)
+        mxq.fp8_gemm_per_tensor(a, sa, b, sb)
+
+    def bw_path():
+        a, sa = mxq.fp8_quantize_blockwise_act(X)
+        b, sb = mxq.fp8_quantize_blockwise_weight(W)
+        mxq.fp8_gemm_blockwise(a, sa, b, sb)
+
+    cold_paths = {}
+    for name, path in (("mx", mx_path), ("per_tensor", pt_path), ("blockwise", bw_path)):
+        ms = cold(path)
+        cold_paths[name] = {"us": ms * 1e3, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12}
+    del flush
     # output error of each format against the FP32 product of the BF16 inputs
     ref = X.float() @ W.float().t()
     rn = ref.norm().item()
@@ -412,6 +451,7 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "blockwise_quant_X_1x128": {"us": t_bx * 1e3, "GB_per_s": gb(nX, 3 + 4 / 128, t_bx)},
         "blockwise_quant_W_128x128": {"us": t_bw * 1e3, "GB_per_s": gb(nW, 3, t_bw)},
         "blockwise_gemm_fwd": {"us": t_bg * 1e3, "TFLOP_per_s": flops / (t_bg * 1e-3) / 1e12},
+        "cold_cache_path_median": cold_paths,
         "relative_output_error_vs_fp32_of_bf16_inputs": errs,
         "vendor_hipblaslt_per_tensor_fp8": vendor,
     }
