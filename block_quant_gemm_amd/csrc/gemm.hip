@@ -1007,7 +1007,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   if (staged) {
     // Full-width BF16 tile: round into LDS (rows of kCStride bytes; the 16
     // bytes of padding spread 16 consecutive rows over the banks), then store
-    // whole rows, 16 bytes per lane, two 512-byte rows per instruction.
+    // whole rows, 16 bytes per lane, two 512-byte rows per instruction.  The
+    // stores are non-temporal: the output is not read again by this kernel,
+    // and kept out of the caches it leaves them to the operand panels.
     barrier();                                      // every wave's loads drained
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1030,9 +1032,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     for (int it = 0; it < 16; ++it) {
       const int row = wave * 32 + it * 2 + rsub;
       if (row < c_rows) {
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
-        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(cbase) + (m0 + row) * g.ldc * 2 +
-                                  n0 * 2 + col * 16) = v;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(smem + row * kCStride + col * 16);
+        __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint8_t*>(cbase) +
+                                    (m0 + row) * g.ldc * 2 + n0 * 2 + col * 16));
       }
     }
     return;
