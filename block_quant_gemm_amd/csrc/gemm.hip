@@ -840,7 +840,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
     barrier();                                      // the k loop's LDS reads are done
     if (cbase) {
       // The gate/up product in BF16 (gate columns to [hct, +128), up columns
-      // to [F + hct, +128)), staged as [256 rows][128 gate | 128 up].
+      // to [F + hct, +128)), staged as [256 rows][128 gate | 128 up], stored
+      // non-temporally like the plain product's output.
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -865,9 +866,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       for (int it = 0; it < 16; ++it) {
         const int row = wave * 32 + it * 2 + rsub;
         if (row < rows_t && hc < F) {
-          const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kCStride + col * 16);
-          *reinterpret_cast<uint4*>(static_cast<uint8_t*>(cbase) + (m0 + row) * g.ldc * 2 +
-                                    gcol * 2) = v;
+          const i32x4 v = *reinterpret_cast<const i32x4*>(smem + row * kCStride + col * 16);
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(
+              static_cast<uint8_t*>(cbase) + (m0 + row) * g.ldc * 2 + gcol * 2));
         }
       }
       barrier();
