@@ -1003,10 +1003,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   //                [n = bn + j*32 + 8*(v/4) + 4*(lane/32) + v%4]
   float mul = 1.0f;
   if (PT) mul = g.pta[group] * g.ptb[group];
-  const bool staged = OUT == MXQ_OUT_BF16 && n0 + TN <= g.N && (g.ldc & 7) == 0 &&
-                      (reinterpret_cast<uintptr_t>(cbase) & 15) == 0;
+  // Staged when the tile's valid columns are whole 16-byte chunks: a full
+  // tile, or a partial one of an output whose width is a multiple of 8.
+  const int64_t c_cols = g.N - n0;                  // valid columns (may exceed TN)
+  const bool staged = OUT == MXQ_OUT_BF16 && (c_cols >= TN || (g.N & 7) == 0) &&
+                      (g.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(cbase) & 15) == 0;
   if (staged) {
-    // Full-width BF16 tile: round into LDS (rows of kCStride bytes; the 16
+    // BF16 tile: round into LDS (rows of kCStride bytes; the 16
     // bytes of padding spread 16 consecutive rows over the banks), then store
     // whole rows, 16 bytes per lane, two 512-byte rows per instruction.  The
     // stores are non-temporal: the output is not read again by this kernel,
@@ -1032,7 +1035,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int row = wave * 32 + it * 2 + rsub;
-      if (row < c_rows) {
+      if (row < c_rows && col * 8 < c_cols) {
         const i32x4 v = *reinterpret_cast<const i32x4*>(smem + row * kCStride + col * 16);
         __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(static_cast<uint8_t*>(cbase) +
                                     (m0 + row) * g.ldc * 2 + n0 * 2 + col * 16));
