@@ -297,6 +297,26 @@ __device__ __forceinline__ uint32_t mx_block_f32(const float (&v)[32], uint32_t 
   return code;
 }
 
+// E8M0 code c as the FP32 scale operand of the scaled conversions, which
+// take its exponent field: 2^(c - 127); 0xFF (a NaN block) turns every
+// converted value into NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t c) { return __builtin_bit_cast(float, c << 23); }
+
+// Eight E4M3 codes (bytes of w0, then w1) times 2^(c - 127) as BF16, element
+// i from byte i.  Exact while the product is a normal or subnormal BF16
+// value with its bits intact: scale codes 3..246.
+__device__ __forceinline__ bf16x8 widen8_bf16(uint32_t w0, uint32_t w1, float s) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  const bf16x4 lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const bf16x4 hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // The MFMA operand of tile row r for one k-step: 16-byte chunks c0 and c1.
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* l, int r, int c0, int c1) {
   const uint4 x = *reinterpret_cast<const uint4*>(l + lds_off(r, c0));
@@ -423,10 +443,16 @@ constexpr int kBlkScaleWords = 320;
 // BLK: blockwise FP32 scales (dense only): 1x128 blocks of A, 128x128 blocks
 // of B; each k-step's product is formed with unit scales and promoted into
 // the FP32 accumulators times its blocks' two scales.
-template <int KIND, bool PT, int OUT, bool SW, bool SWI, bool BLK>
+// XA: exact products (MXQ_ACC_FP32): each 32-block of codes is widened to
+// BF16 with its E8M0 scale folded in (exact for scale codes 3..246, which
+// every finite BF16 block yields unless its largest magnitude is below
+// 2^-116), and multiplied on the BF16 matrix instruction, whose products are
+// exact and whose sums are FP32-accurate.
+template <int KIND, bool PT, int OUT, bool SW, bool SWI, bool BLK, bool XA = false>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   static_assert(!SWI || (KIND == kVarM && OUT == MXQ_OUT_BF16), "SwiGLU product kind");
   static_assert(!BLK || (KIND == kDense && !PT && !SW && !SWI), "blockwise kind");
+  static_assert(!XA || (!SWI && !BLK), "exact-product kind");
   constexpr bool SBYTES = !PT && !SW && !BLK;       // per-step scale-byte loads
   constexpr bool SWIN = !PT && SW && !BLK;          // scale windows
   // [slot][A, B] stages; after the k loop, the staged BF16 output tile
@@ -642,9 +668,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   };
 
   // Fragments and scales of one k-step for this wavefront's 128 x 64 tile.
+  // sa / sb: the scale code each lane passes to the FP8 instruction (block
+  // `half` of the step); with XA, sa / sb hold block 0 and sa1 / sb1 block 1.
   struct Frags {
     i32x8 a[4], b[2];
     uint32_t sa[4], sb[2];
+    uint32_t sa1[4], sb1[2];
   };
   auto read = [&](int32_t s, Frags& f) {
     const uint32_t slot = (uint32_t)((s >> 1) & (kSlots - 1));
@@ -663,33 +692,45 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       f.sb[0] = f.sb[1] = sc[256 + (bn >> 7)];
     } else if (PT) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.sa[i] = 127u;
+      for (int i = 0; i < 4; ++i) f.sa[i] = f.sa1[i] = 127u;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.sb[j] = 127u;
+      for (int j = 0; j < 2; ++j) f.sb[j] = f.sb1[j] = 127u;
     } else if (SBYTES) {
       const uint32_t* sc = ssc + (slot * 2 + ks) * 2 * 2 * TM;
+      const int h0 = XA ? 0 : half;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.sa[i] = sc[(wm * 128 + i * 32 + r32) * 2 + half];
+      for (int i = 0; i < 4; ++i) f.sa[i] = sc[(wm * 128 + i * 32 + r32) * 2 + h0];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.sb[j] = sc[2 * TM + (bn + j * 32 + r32) * 2 + half];
+      for (int j = 0; j < 2; ++j) f.sb[j] = sc[2 * TM + (bn + j * 32 + r32) * 2 + h0];
+      if (XA) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.sa1[i] = sc[(wm * 128 + i * 32 + r32) * 2 + 1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) f.sb1[j] = sc[2 * TM + (bn + j * 32 + r32) * 2 + 1];
+      }
     } else {
       // block 2s + half of row r: window (smis + 2s + half) / 16 relative to
       // the tile, byte (smis + 2s + half) % 16; blocks past the range read as
       // scale code 0 (their codes are zero).
       const int32_t p = s >> 3;
       const uint32_t ps0 = (uint32_t)(p % kWinSlots), ps1 = ps0 == kWinSlots - 1 ? 0 : ps0 + 1;
-      const uint32_t u = (uint32_t)(2 * (s & 7) + half);
-      const bool valid = 2 * (uint32_t)s + half < nblk;
-      const uint32_t ta = A.smis + u, tb = B.smis + u;
-      const uint8_t* wA = reinterpret_cast<const uint8_t*>(ssc) + (ta >> 4 ? ps1 : ps0) * kWinBytes +
-                          (ta & 15) + (wm * 128 + r32) * 16;
-      const uint8_t* wB = reinterpret_cast<const uint8_t*>(ssc) + (tb >> 4 ? ps1 : ps0) * kWinBytes +
-                          kWinBytes / 2 + (tb & 15) + (bn + r32) * 16;
-      const uint32_t keep = valid ? 0xFFu : 0u;     // a mask, so the loads stay unconditional
+      auto window_codes = [&](int hb, uint32_t (&sa)[4], uint32_t (&sb)[2]) {
+        const uint32_t u = (uint32_t)(2 * (s & 7) + hb);
+        const bool valid = 2 * (uint32_t)s + hb < nblk;
+        const uint32_t ta = A.smis + u, tb = B.smis + u;
+        const uint8_t* wA = reinterpret_cast<const uint8_t*>(ssc) +
+                            (ta >> 4 ? ps1 : ps0) * kWinBytes + (ta & 15) + (wm * 128 + r32) * 16;
+        const uint8_t* wB = reinterpret_cast<const uint8_t*>(ssc) +
+                            (tb >> 4 ? ps1 : ps0) * kWinBytes + kWinBytes / 2 + (tb & 15) +
+                            (bn + r32) * 16;
+        const uint32_t keep = valid ? 0xFFu : 0u;   // a mask, so the loads stay unconditional
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.sa[i] = (uint32_t)wA[i * 32 * 16] & keep;
+        for (int i = 0; i < 4; ++i) sa[i] = (uint32_t)wA[i * 32 * 16] & keep;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.sb[j] = (uint32_t)wB[j * 32 * 16] & keep;
+        for (int j = 0; j < 2; ++j) sb[j] = (uint32_t)wB[j * 32 * 16] & keep;
+      };
+      window_codes(XA ? 0 : half, f.sa, f.sb);
+      if (XA) window_codes(1, f.sa1, f.sb1);
     }
   };
   // The 8 MFMAs of one k-step; with ISSUE, this wavefront's share of stage
@@ -728,6 +769,35 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       });
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[3][1][v] = __builtin_fmaf(tp[1][v], sab[3], acc[3][1][v]);
+    } else if constexpr (XA) {
+      asm volatile("" : "+v"(f.sa1[0]), "+v"(f.sa1[1]), "+v"(f.sa1[2]), "+v"(f.sa1[3]),
+                   "+v"(f.sb1[0]), "+v"(f.sb1[1]));
+      // Block HB of the step is dwords 4 HB .. 4 HB + 3 of every fragment (16
+      // codes per lane); each BF16 instruction takes 8 of them per lane, the
+      // same k positions for A and B.  One 32-block at a time keeps the
+      // widened operands within the register budget.
+      static_for<2>([&](auto hbc) {
+        constexpr int HB = decltype(hbc)::value;
+        bf16x8 bw[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float sc = e8m0_f32(HB ? f.sb1[j] : f.sb[j]);
+          bw[j][0] = widen8_bf16(f.b[j][4 * HB], f.b[j][4 * HB + 1], sc);
+          bw[j][1] = widen8_bf16(f.b[j][4 * HB + 2], f.b[j][4 * HB + 3], sc);
+        }
+        static_for<4>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          const float sc = e8m0_f32(HB ? f.sa1[I] : f.sa[I]);
+          const bf16x8 a0 = widen8_bf16(f.a[I][4 * HB], f.a[I][4 * HB + 1], sc);
+          const bf16x8 a1 = widen8_bf16(f.a[I][4 * HB + 2], f.a[I][4 * HB + 3], sc);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j][0], a0, acc[I][j], 0, 0, 0);
+            acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[j][1], a1, acc[I][j], 0, 0, 0);
+          }
+          if constexpr (ISSUE) stage_dma(u, HB * 4 + I);
+        });
+      });
     } else {
     static_for<8>([&](auto k) {
       constexpr int K = decltype(k)::value, i = K / 2, j = K % 2;
@@ -1061,9 +1131,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   }
 }
 
-template <int KIND, bool PT, int OUT, bool SW>
+template <int KIND, bool PT, int OUT, bool SW, bool XA>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmArgs g) {
-  gemm_body<KIND, PT, OUT, SW, false, false>(g);
+  gemm_body<KIND, PT, OUT, SW, false, false, XA>(g);
 }
 
 template <bool SW>
@@ -1095,28 +1165,37 @@ using namespace mxq;
 
 static inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-template <int KIND, bool PT, bool SW>
+template <int KIND, bool PT, bool SW, bool XA>
 static void launch_kernel(const GemmArgs& g, uint32_t blocks, int out, hipStream_t stream) {
   if (out == MXQ_OUT_BF16)
-    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_BF16, SW>), dim3(blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_BF16, SW, XA>), dim3(blocks), dim3(kThreads), 0,
                        stream, g);
   else
-    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_FP32, SW>), dim3(blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_gemm<KIND, PT, MXQ_OUT_FP32, SW, XA>), dim3(blocks), dim3(kThreads), 0,
                        stream, g);
+}
+
+template <int KIND, bool PT, bool SW>
+static void launch_accum(const GemmArgs& g, uint32_t blocks, int out, int accum,
+                         hipStream_t stream) {
+  if (accum == MXQ_ACC_FP32)
+    launch_kernel<KIND, PT, SW, true>(g, blocks, out, stream);
+  else
+    launch_kernel<KIND, PT, SW, false>(g, blocks, out, stream);
 }
 
 // Scale windows need both operands' scale row strides to be multiples of 16.
 template <int KIND, bool PT>
-static int launch_gemm(GemmArgs& g, int64_t blocks, int out, hipStream_t stream) {
+static int launch_gemm(GemmArgs& g, int64_t blocks, int out, int accum, hipStream_t stream) {
   if (blocks == 0) return MXQ_OK;
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   g.nblocks = (uint32_t)blocks;
   if constexpr (PT)
-    launch_kernel<KIND, PT, false>(g, (uint32_t)blocks, out, stream);
+    launch_accum<KIND, PT, false>(g, (uint32_t)blocks, out, accum, stream);
   else if (g.ldsa % 16 == 0 && g.ldsb % 16 == 0)
-    launch_kernel<KIND, PT, true>(g, (uint32_t)blocks, out, stream);
+    launch_accum<KIND, PT, true>(g, (uint32_t)blocks, out, accum, stream);
   else
-    launch_kernel<KIND, PT, false>(g, (uint32_t)blocks, out, stream);
+    launch_accum<KIND, PT, false>(g, (uint32_t)blocks, out, accum, stream);
   return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
@@ -1165,9 +1244,8 @@ extern "C" int mx_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, in
     if ((st = check_operand(a, a_scale, lda, ldsa, K, true))) return st;
     if ((st = check_operand(b, b_scale, ldb, ldsb, K, true))) return st;
   }
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;   // exact-product mode: not built yet
   GemmArgs g = make_args(a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, M, N, K, c, ldc);
-  return launch_gemm<kDense, false>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype,
+  return launch_gemm<kDense, false>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype, accum,
                                     stream);
 }
 
@@ -1184,10 +1262,9 @@ extern "C" int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64
     if ((st = check_operand(a, a_scale, lda, 0, K, false))) return st;
     if ((st = check_operand(b, b_scale, ldb, 0, K, false))) return st;
   }
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   GemmArgs g = make_args(a, nullptr, lda, 0, b, nullptr, ldb, 0, M, N, K, c, ldc);
   g.pta = a_scale; g.ptb = b_scale;
-  return launch_gemm<kDense, true>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype,
+  return launch_gemm<kDense, true>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype, accum,
                                    stream);
 }
 
@@ -1243,12 +1320,11 @@ extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t
   }
   if (b_estride < 0 || bs_estride < 0) return MXQ_ERR_SHAPE;
   if (b_estride % 16 != 0) return MXQ_ERR_ALIGN;
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   GemmArgs g = make_args(a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, M, N, K, c, ldc);
   g.b_estride = b_estride; g.bs_estride = bs_estride;
   g.offsets = offsets; g.E = E;
   const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
-  return launch_gemm<kVarM, false>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
+  return launch_gemm<kVarM, false>(g, mtiles * (int64_t)g.tiles_n, out_dtype, accum, stream);
 }
 
 extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, int64_t lda,
@@ -1264,6 +1340,8 @@ extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, 
   if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
   if (!offsets) return MXQ_ERR_NULL;
   if (F % 32 != 0 || K % 32 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  // h's column copy must hold every row after each group is padded to 32
+  if (M > 0 && M_cap < M + 31LL * E) return MXQ_ERR_SHAPE;
   if (F == 0) return MXQ_OK;
   if (M > 0 && (!hq || !hs || (M_cap > 0 && (!hqT || !hsT)))) return MXQ_ERR_NULL;
   if (ldhq < F || ldhs < F / 32 || ldhqT < M_cap || ldhsT < M_cap / 32) return MXQ_ERR_SHAPE;
@@ -1364,13 +1442,12 @@ extern "C" int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scale
   }
   if (b_estride < 0) return MXQ_ERR_SHAPE;
   if (b_estride % 16 != 0) return MXQ_ERR_ALIGN;
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   GemmArgs g = make_args(a, nullptr, lda, 0, b, nullptr, ldb, 0, M, N, K, c, ldc);
   g.b_estride = b_estride;
   g.pta = a_scales; g.ptb = b_scales;
   g.offsets = offsets; g.E = E;
   const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
-  return launch_gemm<kVarM, true>(g, mtiles * (int64_t)g.tiles_n, out_dtype, stream);
+  return launch_gemm<kVarM, true>(g, mtiles * (int64_t)g.tiles_n, out_dtype, accum, stream);
 }
 
 extern "C" int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* a_scales,
@@ -1389,12 +1466,11 @@ extern "C" int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* 
     return MXQ_ERR_ALIGN;
   const int64_t cap = lda_t < ldb_t ? lda_t : ldb_t;    // token capacity of both operands
   if (!fits32(lda_t, cap) || !fits32(ldb_t, cap)) return MXQ_ERR_SHAPE;
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   GemmArgs g = make_args(at, nullptr, lda_t, 0, bt, nullptr, ldb_t, 0, N, K, cap, c, ldc);
   g.pta = a_scales; g.ptb = b_scales;
   g.offsets = offsets_padded; g.E = E;
   const int64_t blocks = (int64_t)E * ((N + TM - 1) / TM) * g.tiles_n;
-  return launch_gemm<kVarK, true>(g, blocks, out_dtype, stream);
+  return launch_gemm<kVarK, true>(g, blocks, out_dtype, accum, stream);
 }
 
 extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale, int64_t lda_t,
@@ -1417,11 +1493,10 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale,
   if (!fits32(lda_t, cap) || !fits32(ldb_t, cap) || !fits32(ldsa_t, cap / 32) ||
       !fits32(ldsb_t, cap / 32))
     return MXQ_ERR_SHAPE;
-  if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   // For this kind: M = rows of dW (N), N = columns of dW (K), K = token capacity.
   GemmArgs g = make_args(at, at_scale, lda_t, ldsa_t, bt, bt_scale, ldb_t, ldsb_t, N, K, cap, c,
                          ldc);
   g.offsets = offsets_padded; g.E = E;
   const int64_t blocks = (int64_t)E * ((N + TM - 1) / TM) * g.tiles_n;
-  return launch_gemm<kVarK, false>(g, blocks, out_dtype, stream);
+  return launch_gemm<kVarK, false>(g, blocks, out_dtype, accum, stream);
 }

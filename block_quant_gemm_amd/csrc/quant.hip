@@ -787,19 +787,26 @@ extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int6
   return launch_status();
 }
 
+// Columns a grouped column copy may need: every group padded to a multiple
+// of 32 adds at most 31 (the offsets are on the device, so the bound is
+// checked, not the padded total).  No groups: M rounded up to 32.  An empty
+// input needs nothing.
+static int64_t padded_capacity(int64_t M, int32_t E) {
+  if (M <= 0) return 0;
+  return E > 0 ? M + 31LL * E : (M + 31) / 32 * 32;
+}
+
 extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    const int64_t* offsets, int32_t E, uint8_t* qT, int64_t ldqT,
                                    int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
                                    int64_t* offsets_padded, hipStream_t stream) {
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (offsets && (E < 1 || E > kColMaxGroupsLds)) return MXQ_ERR_SHAPE;
+  if (M_cap < padded_capacity(M, offsets ? E : 0)) return MXQ_ERR_SHAPE;
   if (K == 0 || M_cap == 0) return MXQ_OK;
   if (!qT || !scaleT || (M > 0 && !x)) return MXQ_ERR_NULL;
   if (K % 8 != 0 || M_cap % 32 != 0 || ldqT < M_cap || ldsT < M_cap / 32 || ldx < K)
     return MXQ_ERR_SHAPE;
-  int64_t need = offsets ? M + 31LL * E : (M + 31) / 32 * 32;
-  if (!offsets && M_cap < need) return MXQ_ERR_SHAPE;
-  (void)need;
   if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
     return MXQ_ERR_ALIGN;
   const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
@@ -818,12 +825,14 @@ extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t
                                 int64_t* offsets_padded, hipStream_t stream) {
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (offsets && (E < 1 || E > kColMaxGroupsLds)) return MXQ_ERR_SHAPE;
+  // every row must land in the column copy: the row copy is written from the
+  // same column tiles
+  if (M_cap < padded_capacity(M, offsets ? E : 0)) return MXQ_ERR_SHAPE;
   if (K == 0 || M_cap == 0) return MXQ_OK;
   if (!qT || !scaleT || (M > 0 && (!x || !q || !scale))) return MXQ_ERR_NULL;
   if (K % 32 != 0 || M_cap % 32 != 0 || ldqT < M_cap || ldsT < M_cap / 32 || ldx < K ||
       ldq < K || lds < K / 32)
     return MXQ_ERR_SHAPE;
-  if (!offsets && M_cap < (M + 31) / 32 * 32) return MXQ_ERR_SHAPE;
   if (ldqT % 16 != 0 || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(qT, 16) ||
       (x && !aligned(x, 16)) || (q && !aligned(q, 16)))
     return MXQ_ERR_ALIGN;
@@ -923,7 +932,7 @@ static int quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, i
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
   if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
-  if (K % 8 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  if (K % 8 != 0 || M_cap % 32 != 0 || M_cap < padded_capacity(M, E)) return MXQ_ERR_SHAPE;
   if (K > 0 && M_cap > 0) {
     if (!qT || (M > 0 && !x)) return MXQ_ERR_NULL;
     if (ldqT < M_cap || (M > 0 && ldx < K)) return MXQ_ERR_SHAPE;
@@ -982,7 +991,7 @@ extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kPgMaxGroups || E > kColMaxGroupsLds) return MXQ_ERR_SHAPE;
   if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
-  if (K % 8 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
+  if (K % 8 != 0 || M_cap % 32 != 0 || M_cap < padded_capacity(M, E)) return MXQ_ERR_SHAPE;
   if (K > 0 && M_cap > 0) {
     if (!qT || (M > 0 && (!x || !q))) return MXQ_ERR_NULL;
     if (ldqT < M_cap || (M > 0 && (ldx < K || ldq < K))) return MXQ_ERR_SHAPE;

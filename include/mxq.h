@@ -101,10 +101,11 @@ MXQ_API int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t
  *              32 along M.  Each group is padded with zero rows to a multiple
  *              of 32, so group g occupies columns [poff[g], poff[g+1]) with
  *              poff[g+1] - poff[g] = ceil(m_g/32)*32.
- *   M_cap    : number of output columns written; must be >= the padded
- *              total, which is at most M + 31*E (M rounded up to 32 when
- *              offsets is NULL).  Columns in [padded total, M_cap) are
- *              zero-filled (codes and scales).
+ *   M_cap    : number of output columns written.  The padded total is
+ *              known only on the device, so M_cap must be >= its bound
+ *              M + 31*E (M rounded up to 32 when offsets is NULL), else
+ *              MXQ_ERR_SHAPE (M == 0 needs nothing).  Columns in
+ *              [padded total, M_cap) are zero-filled (codes and scales).
  *   scaleT   : device, E8M0 [K, ldsT], ldsT >= M_cap/32.
  *   offsets_padded : device int64 [E+1] receiving poff, or NULL.
  * Requires K % 8 == 0, M_cap % 32 == 0, ldqT >= M_cap, ldqT % 16 == 0,
@@ -194,7 +195,8 @@ MXQ_API int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int6
  * zero-filled.
  *   x, offsets, E, scales, workspace : as fp8_quantize_per_group.
  *   qT            : device, E4M3 [K, M_cap], row stride ldqT bytes (% 16 == 0),
- *                   16-byte aligned; M_cap % 32 == 0 (M + 31*E is always enough).
+ *                   16-byte aligned; M_cap % 32 == 0 and M_cap >= M + 31*E
+ *                   (the bound of the padded total; else MXQ_ERR_SHAPE).
  *   offsets_padded: device int64 [E+1] receiving the padded offsets, or NULL.
  */
 MXQ_API int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -240,8 +242,8 @@ MXQ_API int fp8_quantize_per_group_colwise_amax(const uint16_t* x, int64_t M, in
  *   q, ldq   : device E4M3 [M, K] (ldq % 8 == 0, 8-byte aligned).
  *   qT, ldqT, M_cap, scales, offsets_padded : as fp8_quantize_per_group_colwise.
  *   workspace: mxq_workspace_size(MXQ_WS_PER_GROUP, M, E, 0, 0) bytes.
- * Rows outside every group, and columns past M_cap, are not written (M_cap >=
- * M + 31*E holds every group's padding).
+ * Rows outside every group are not written; M_cap >= M + 31*E is required
+ * (MXQ_ERR_SHAPE otherwise), so every row lands in both copies.
  */
 MXQ_API int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                 const int64_t* offsets, int32_t E, const float* amax,
@@ -385,8 +387,8 @@ MXQ_API int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t ld
  *   hqT, hsT    : device, h's grouped column copy: codes [F, M_cap] (stride
  *                 ldhqT), scales [F, M_cap/32] (stride ldhsT); each group zero-
  *                 padded to a multiple of 32 rows, as mx_quantize_colwise with
- *                 offsets; columns past M_cap are not written (M_cap >= M + 31*E
- *                 holds every padding).
+ *                 offsets; M_cap >= M + 31*E is required when M > 0 (the
+ *                 bound of the padded total; MXQ_ERR_SHAPE otherwise).
  *   offsets_padded : device int64 [E+1] receiving the padded offsets, or NULL.
  * Requires F % 32 == 0, K % 32 == 0, M_cap % 32 == 0, ldhq and ldhqT multiples
  * of 16 with 16-byte aligned hq, hqT; ldgu % 8 == 0 and 16-byte aligned gu; the

@@ -11,6 +11,7 @@ import torch
 
 from block_quant_gemm_amd import mxq, workloads
 from oracle import gemm, mx
+from tests import fp8_mode as f8
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -43,9 +44,9 @@ def _check_sampled(c, aq, asc, bq, bsc, rows, cols, crows=None, ccols=None):
     bh, bsh = host(bq[ci]), host(bsc[ci])
     idx = np.arange(len(rows))
     Y, S = gemm.gemm_ref_entries(mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh), idx, idx)
-    Tb = gemm.fp8_mfma_truncation_bound(ah, ash, bh, bsh, idx, idx)
+    Tb = f8.fp8_mfma_truncation_bound(ah, ash, bh, bsh, idx, idx)
     ch = host(c)[crows, ccols]
-    ok = gemm.check_bf16_extra(ch, Y, S, Tb)
+    ok = f8.check_bf16_extra(ch, Y, S, Tb)
     if not ok.all():
         bad = np.nonzero(~ok)[0][:8]
         raise AssertionError(f"outputs {list(zip(crows[bad], ccols[bad]))}: "
@@ -119,9 +120,9 @@ def test_block_routed_experts_98304_rows():
         b = mx.mx_dequantize(xh[k[i]:k[i] + 1, lo:hi], xsh[k[i]:k[i] + 1, lo // 32:hi // 32])
         y, s = gemm.gemm_ref(a, b)
         Y[i], S[i] = y[0, 0], s[0, 0]
-        Tb[i] = gemm.fp8_mfma_truncation_bound(uh[n[i]:n[i] + 1, lo:hi],
+        Tb[i] = f8.fp8_mfma_truncation_bound(uh[n[i]:n[i] + 1, lo:hi],
                                                ush[n[i]:n[i] + 1, lo // 32:hi // 32],
                                                xh[k[i]:k[i] + 1, lo:hi],
                                                xsh[k[i]:k[i] + 1, lo // 32:hi // 32])[0, 0]
     ch = host(dw)[e, n, k]
-    assert gemm.check_bf16_extra(ch, Y, S, Tb).all()
+    assert f8.check_bf16_extra(ch, Y, S, Tb).all()

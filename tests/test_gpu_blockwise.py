@@ -11,6 +11,7 @@ import torch
 from block_quant_gemm_amd import mxq, workloads
 from oracle import blockwise as bw
 from oracle import codec, gemm
+from tests import fp8_mode as f8
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +80,7 @@ def _allowance(qa, sa, qw, sw, rows, cols):
     T = np.zeros(len(rows))
     for b in range(K // 128):
         ks = slice(128 * b, 128 * b + 128)
-        tb = gemm.fp8_mfma_truncation_bound(qa[rows, ks], ones, qw[cols, ks], ones, idx, idx)
+        tb = f8.fp8_mfma_truncation_bound(qa[rows, ks], ones, qw[cols, ks], ones, idx, idx)
         T += tb * sa[rows, b].astype(np.float64) * sw[cols // 128, b].astype(np.float64)
     return T
 
@@ -100,9 +101,9 @@ def test_blockwise_gemm(M, N, K, out):
     cols = np.tile(np.arange(N), M)
     T = _allowance(qa, sa, qw, sw, rows, cols).reshape(M, N)
     if out == mxq.OUT_FP32:
-        ok = gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T)
+        ok = f8.check_fp32_extra(host(c).astype(np.float64), Y, S, T)
     else:
-        ok = gemm.check_bf16_extra(host(c), Y, S, T)
+        ok = f8.check_bf16_extra(host(c), Y, S, T)
     say(f"  within tolerance: {ok.mean():.6f}")
     assert ok.all()
 
@@ -132,4 +133,4 @@ def test_blockwise_dense_ffn_forward_sampled():
     idx = np.arange(3000)
     Y, S = gemm.gemm_ref_entries(A, B, idx, idx)
     T = _allowance(qa, sa, qw, sw, rows, cols)
-    assert gemm.check_bf16_extra(host(c)[rows, cols], Y, S, T).all()
+    assert f8.check_bf16_extra(host(c)[rows, cols], Y, S, T).all()

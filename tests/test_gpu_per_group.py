@@ -9,9 +9,12 @@ import torch
 
 from block_quant_gemm_amd import mxq, workloads
 from oracle import codec, gemm, per_tensor
+from tests import fp8_mode as f8
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
+
+ACCS = [mxq.ACC_FP32, mxq.ACC_MFMA_FP8]
 
 
 def _quant(bits, offs):
@@ -111,7 +114,7 @@ def _gemm_allowance(ah, bh, sa, sb, offs, N):
     for e in range(E):
         lo, hi = int(offs[e]), int(offs[e + 1])
         if hi > lo:
-            T[lo:hi] = gemm.fp8_mfma_truncation_bound(
+            T[lo:hi] = f8.fp8_mfma_truncation_bound(
                 ah[lo:hi], ones_a[lo:hi], bh[e * N:(e + 1) * N], ones_b) * \
                 float(sa[e]) * float(sb[e])
     return T
@@ -123,8 +126,9 @@ def _gemm_allowance(ah, bh, sa, sb, offs, N):
     ([5], 32, 32),
 ])
 @pytest.mark.parametrize("out", [mxq.OUT_BF16, mxq.OUT_FP32])
-def test_per_group_grouped_gemm(counts, N, K, out):
-    say(f"per-group grouped gemm counts={counts} N={N} K={K} out={out}")
+@pytest.mark.parametrize("accum", ACCS)
+def test_per_group_grouped_gemm(counts, N, K, out, accum):
+    say(f"per-group grouped gemm counts={counts} N={N} K={K} out={out} accum={accum}")
     counts = np.array(counts, np.int64)
     offs = workloads.offsets_from_counts(counts)
     E, M = len(counts), int(counts.sum())
@@ -135,17 +139,12 @@ def test_per_group_grouped_gemm(counts, N, K, out):
     aq, sa, ah, sah = _quant(a, offs)
     wq, sw, wh, swh = _quant(w, woffs)
     c = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(E, N, K), sw, to_dev(offs),
-                                       out_dtype=out)
+                                       out_dtype=out, accum=accum)
     A = per_tensor.pg_dequantize(ah, sah, offs)
     B = per_tensor.pg_dequantize(wh, swh, woffs).reshape(E, N, K)
     Y, S = gemm.grouped_gemm_ref(A, B, offs)
-    T = _gemm_allowance(ah, wh, sah, swh, offs, N) + 2.0 ** -23 * np.abs(Y)
-    if out == mxq.OUT_FP32:
-        ok = gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T)
-    else:
-        ok = gemm.check_bf16_extra(host(c), Y, S, T)
-    say(f"  elements {ok.size}: within tolerance {ok.mean():.6f}")
-    assert ok.all()
+    f8.accept(host(c), Y, S, out == mxq.OUT_FP32, accum == mxq.ACC_FP32,
+              lambda: _gemm_allowance(ah, wh, sah, swh, offs, N) + 2.0 ** -23 * np.abs(Y))
 
 
 def test_per_group_one_group_equals_per_tensor():
@@ -165,17 +164,19 @@ def test_per_group_one_group_equals_per_tensor():
     assert torch.equal(cg, cd)
 
 
-def test_per_group_gate_up_full_size_sampled():
+@pytest.mark.parametrize("accum", ACCS)
+def test_per_group_gate_up_full_size_sampled(accum):
     """MoE gate_up forward at full size with per-expert scales: 49152 rows,
     64 experts, W_gu [64, 2816, 2048]; 2000 sampled outputs."""
-    say("per-group grouped gate_up 49152 x 2816 x 2048")
+    say(f"per-group grouped gate_up 49152 x 2816 x 2048 accum={accum}")
     d = workloads.moe_forward(0)
     offs, E = d["offsets"], 64
     w = d["W_gu"].reshape(E * 2816, 2048)
     woffs = np.arange(E + 1, dtype=np.int64) * 2816
     aq, sa, ah, sah = _quant(d["X"], offs)
     wq, sw, wh, swh = _quant(w, woffs)
-    c = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(E, 2816, 2048), sw, to_dev(offs))
+    c = mxq.fp8_grouped_gemm_per_group(aq, sa, wq.view(E, 2816, 2048), sw, to_dev(offs),
+                                       accum=accum)
     rng = np.random.default_rng(2)
     rows = rng.integers(0, 49152, 2000)
     n = rng.integers(0, 2816, 2000)
@@ -186,10 +187,10 @@ def test_per_group_gate_up_full_size_sampled():
     B = per_tensor.pt_dequantize(wh[cols], np.float32(1.0)) * swh[e].astype(np.float64)[:, None]
     Y, S = gemm.gemm_ref_entries(A, B, idx, idx)
     ones = np.full((len(rows), 64), 127, np.uint8)
-    T = gemm.fp8_mfma_truncation_bound(ah[rows], ones, wh[cols], ones, idx, idx) * \
-        sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y)
     ch = host(c)[rows, n]
-    assert gemm.check_bf16_extra(ch, Y, S, T).all()
+    f8.accept(ch, Y, S, False, accum == mxq.ACC_FP32,
+              lambda: f8.fp8_mfma_truncation_bound(ah[rows], ones, wh[cols], ones, idx, idx) *
+              sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y))
 
 
 # ---------------------------------------------------------------------------
@@ -284,8 +285,9 @@ def _dequant_colwise(qTh, sh, ph):
     ([300, 0, 45, 513], 296, 768),
 ])
 @pytest.mark.parametrize("out", [mxq.OUT_BF16, mxq.OUT_FP32])
-def test_per_group_wgrad(counts, N, K, out):
-    say(f"per-group wgrad counts={counts} N={N} K={K} out={out}")
+@pytest.mark.parametrize("accum", ACCS)
+def test_per_group_wgrad(counts, N, K, out, accum):
+    say(f"per-group wgrad counts={counts} N={N} K={K} out={out} accum={accum}")
     counts = np.array(counts, np.int64)
     offs = workloads.offsets_from_counts(counts)
     E, T = len(counts), int(counts.sum())
@@ -294,7 +296,7 @@ def test_per_group_wgrad(counts, N, K, out):
     x = workloads.bf16_normal((T, K), 1.0, seed=T + K, name="pgwx")
     aT, sa, poff, aTh, sah, ph = _colwise(dy, offs)
     bT, sb, _, bTh, sbh, _ = _colwise(x, offs)
-    c = mxq.fp8_grouped_gemm_wgrad_per_group(aT, sa, bT, sb, poff, out_dtype=out)
+    c = mxq.fp8_grouped_gemm_wgrad_per_group(aT, sa, bT, sb, poff, out_dtype=out, accum=accum)
     A, B = _dequant_colwise(aTh, sah, ph), _dequant_colwise(bTh, sbh, ph)
     Y, S = gemm.grouped_wgrad_ref(A[:, :int(ph[-1])], B[:, :int(ph[-1])], ph)
     Tb = np.zeros_like(Y)
@@ -303,23 +305,19 @@ def test_per_group_wgrad(counts, N, K, out):
         if hi > lo:
             ones_a = np.full((N, (hi - lo) // 32), 127, np.uint8)
             ones_b = np.full((K, (hi - lo) // 32), 127, np.uint8)
-            Tb[e] = gemm.fp8_mfma_truncation_bound(aTh[:, lo:hi], ones_a, bTh[:, lo:hi],
+            Tb[e] = f8.fp8_mfma_truncation_bound(aTh[:, lo:hi], ones_a, bTh[:, lo:hi],
                                                    ones_b) * float(sah[e]) * float(sbh[e])
     Tb = Tb + 2.0 ** -23 * np.abs(Y)
-    if out == mxq.OUT_FP32:
-        ok = gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, Tb)
-    else:
-        ok = gemm.check_bf16_extra(host(c), Y, S, Tb)
-    say(f"  elements {ok.size}: within tolerance {ok.mean():.6f}")
-    assert ok.all()
+    f8.accept(host(c), Y, S, out == mxq.OUT_FP32, accum == mxq.ACC_FP32, Tb)
     for e in np.nonzero(counts == 0)[0]:
         assert torch.all(c[e] == 0)
 
 
-def test_per_group_dgrad_with_transposed_weights():
+@pytest.mark.parametrize("accum", ACCS)
+def test_per_group_dgrad_with_transposed_weights(accum):
     """Data gradient dX = dY · W_e per expert: the weights' transposed
     per-expert copy read in place through per-expert strides."""
-    say("per-group dgrad")
+    say(f"per-group dgrad accum={accum}")
     counts = np.array([40, 0, 130, 77], np.int64)
     offs = workloads.offsets_from_counts(counts)
     E, M, N, K = 4, int(counts.sum()), 192, 320     # W_e [N, K]; dY [M, N]; dX [M, K]
@@ -329,7 +327,8 @@ def test_per_group_dgrad_with_transposed_weights():
     wT, sw, _, wTh, swh, wph = _colwise(w, woffs)    # [K, E*N]
     gq, sg, gh, sgh = _quant(dy, offs)
     bview = wT[:, :E * N].view(K, E, N).permute(1, 0, 2)  # [E, K, N], expert stride N
-    c = mxq.fp8_grouped_gemm_per_group(gq, sg, bview, sw, to_dev(offs), out_dtype=mxq.OUT_FP32)
+    c = mxq.fp8_grouped_gemm_per_group(gq, sg, bview, sw, to_dev(offs), out_dtype=mxq.OUT_FP32,
+                                       accum=accum)
     A = per_tensor.pg_dequantize(gh, sgh, offs)
     Bt = _dequant_colwise(wTh, swh, wph)             # [K, E*N]
     B = np.stack([Bt[:, e * N:(e + 1) * N] for e in range(E)])   # [E, K, N]
@@ -340,11 +339,11 @@ def test_per_group_dgrad_with_transposed_weights():
     for e in range(E):
         lo, hi = int(offs[e]), int(offs[e + 1])
         if hi > lo:
-            T[lo:hi] = gemm.fp8_mfma_truncation_bound(gh[lo:hi], onesa[lo:hi],
+            T[lo:hi] = f8.fp8_mfma_truncation_bound(gh[lo:hi], onesa[lo:hi],
                                                       wTh[:, e * N:(e + 1) * N], onesb) * \
                 float(sgh[e]) * float(swh[e])
     T = T + 2.0 ** -23 * np.abs(Y)
-    assert gemm.check_fp32_extra(host(c).astype(np.float64), Y, S, T).all()
+    f8.accept(host(c), Y, S, True, accum == mxq.ACC_FP32, T)
 
 
 # ---------------------------------------------------------------------------

@@ -24,6 +24,7 @@ import torch
 from block_quant_gemm_amd import mxq, workloads
 from oracle import gemm, mx
 from oracle import swiglu as sw
+from tests import fp8_mode as f8
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 from tests.mx_interval import mx_valid
 from tests.test_gpu_gemm import _relayout_scales
@@ -64,7 +65,7 @@ def _reference(offs, xq, xs, wq, ws, F):
     rows = np.repeat(np.arange(M), 2 * F)
     expert = np.searchsorted(offs, np.arange(M), side="right") - 1
     cols = np.repeat(expert, 2 * F) * 2 * F + np.tile(np.arange(2 * F), M)
-    T = gemm.fp8_mfma_truncation_bound(xq, xs, wq, ws, rows, cols).reshape(M, 2 * F)
+    T = f8.fp8_mfma_truncation_bound(xq, xs, wq, ws, rows, cols).reshape(M, 2 * F)
     return Y, S, T
 
 
@@ -137,7 +138,7 @@ def test_swiglu_product(counts, F, K, layout):
     offs, xq, xs, wq, ws = _operands(counts, F, K, seed=len(counts) * 31 + F + K)
     gu, hq, hs, hqT, hsT, poff = _run(offs, xq, xs, wq, ws, F, layout)
     Y, S, T = _reference(offs, xq, xs, wq, ws, F)
-    ok = gemm.check_bf16_extra(gu, Y, S, T)
+    ok = f8.check_bf16_extra(gu, Y, S, T)
     say(f"  gate/up BF16 within tolerance: {ok.mean():.6f}")
     assert ok.all()
     _check_h(offs, Y, S, T, F, hq, hs, hqT, hsT, poff)
@@ -161,7 +162,7 @@ def test_swiglu_product_large_gate_values():
     g = Y[:, :96]
     say(f"  gate range [{g.min():.1f}, {g.max():.1f}]")
     assert g.min() < -88 and g.max() > 88
-    assert gemm.check_bf16_extra(gu, Y, S, T).all()
+    assert f8.check_bf16_extra(gu, Y, S, T).all()
     _check_h(offs, Y, S, T, 96, hq, hs, hqT, hsT, poff)
 
 
@@ -198,7 +199,7 @@ def _sampled_blocks_check(offs, xq, xs, wq, ws, F, hq, hs, hqT, hsT, poff, rng, 
             Bv = mx.mx_dequantize(wq[wr], ws[wr])
             idx = np.arange(len(rows))
             Y, S = gemm.gemm_ref_entries(A, Bv, idx, idx)
-            T = gemm.fp8_mfma_truncation_bound(xq[rows], xs[rows], wq[wr], ws[wr], idx, idx)
+            T = f8.fp8_mfma_truncation_bound(xq[rows], xs[rows], wq[wr], ws[wr], idx, idx)
             out.append((Y, gemm.tolerance(S) + T))
         return out
 
@@ -260,7 +261,7 @@ def test_swiglu_moe_gate_up_full_size_sampled():
     A = mx.mx_dequantize(xq[r], xs[r])
     Bv = mx.mx_dequantize(wq[e * 2 * F + n], ws[e * 2 * F + n])
     Y, S = gemm.gemm_ref_entries(A, Bv, idx, idx)
-    T = gemm.fp8_mfma_truncation_bound(xq[r], xs[r], wq[e * 2 * F + n], ws[e * 2 * F + n],
+    T = f8.fp8_mfma_truncation_bound(xq[r], xs[r], wq[e * 2 * F + n], ws[e * 2 * F + n],
                                        idx, idx)
-    assert gemm.check_bf16_extra(guh[r, n], Y, S, T).all()
+    assert f8.check_bf16_extra(guh[r, n], Y, S, T).all()
     _sampled_blocks_check(offs, xq, xs, wq, ws, F, hq, hs, hqT, hsT, poff, rng)

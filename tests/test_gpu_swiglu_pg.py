@@ -14,6 +14,7 @@ import pytest
 
 from block_quant_gemm_amd import mxq, workloads
 from oracle import codec, gemm, per_tensor
+from tests import fp8_mode as f8
 from tests.gpu_helpers import host, say, to_dev, to_dev_bf16
 from tests.test_gpu_per_group import _gemm_allowance
 from tests.test_gpu_swiglu import h_bounds
@@ -102,7 +103,7 @@ def test_per_group_swiglu_product(counts, F, K):
     B = per_tensor.pg_dequantize(wq, swt, woffs).reshape(E, 2 * F, K)
     Y, S = gemm.grouped_gemm_ref(A, B, offs)
     T = _gemm_allowance(aq, wq, sa, swt, offs, 2 * F) + 2.0 ** -23 * np.abs(Y)
-    assert gemm.check_bf16_extra(guh, Y, S, T).all()
+    assert f8.check_bf16_extra(guh, Y, S, T).all()
     dY = gemm.tolerance(S) + T
     lo, hi = h_bounds(Y[:, :F], Y[:, F:], dY[:, :F], dY[:, F:])
     hv = codec.bf16_bits_to_f64(hh)
@@ -168,14 +169,14 @@ def test_per_group_swiglu_full_size_sampled():
         B = per_tensor.pt_dequantize(wh[wrows], np.float32(1.0)) * swh[e].astype(np.float64)[:, None]
         Y, S = gemm.gemm_ref_entries(A, B, idx, idx)
         ones = np.full((len(rows), K // 32), 127, np.uint8)
-        T = gemm.fp8_mfma_truncation_bound(ah[rows], ones, wh[wrows], ones, idx, idx) * \
+        T = f8.fp8_mfma_truncation_bound(ah[rows], ones, wh[wrows], ones, idx, idx) * \
             sah[e].astype(np.float64) * swh[e].astype(np.float64) + 2.0 ** -23 * np.abs(Y)
         return Y, gemm.tolerance(S) + T, S, T
 
     r, n = rng.integers(0, M, 600), rng.integers(0, 2 * F, 600)
     e = np.searchsorted(offs, r, side="right") - 1
     Y, _, S, T = ref(r, e * 2 * F + n)
-    assert gemm.check_bf16_extra(guh[r, n], Y, S, T).all()
+    assert f8.check_bf16_extra(guh[r, n], Y, S, T).all()
     r, c = rng.integers(0, M, 1500), rng.integers(0, F, 1500)
     e = np.searchsorted(offs, r, side="right") - 1
     g, dg, _, _ = ref(r, e * 2 * F + c)

@@ -24,6 +24,25 @@ def lib():
     return mxq.load()
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0        # counts devices without initialising one
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="module")
+def host_only_lib(lib):
+    """The library, for calls that pass fake device addresses and rely on the
+    host-side checks rejecting them before any launch.  Where a GPU is
+    visible these never run: a regression in a check would launch a kernel
+    on the fake address."""
+    if _gpu_visible():
+        pytest.skip("passes fake device addresses; runs only where no GPU is visible")
+    return lib
+
+
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
     assert len(names) >= 11
@@ -38,7 +57,8 @@ def test_version_and_status_strings(lib):
     assert lib.mxq_status_string(3).startswith(b"misaligned")
 
 
-def test_host_validation_errors(lib):
+def test_host_validation_errors(host_only_lib):
+    lib = host_only_lib
     P = 4096  # a fake, never-dereferenced 16-byte-aligned address
     # negative / inconsistent sizes
     assert lib.mx_quantize_rowwise(P, -1, 32, 32, P, 32, P, 1, None) == 2
@@ -50,6 +70,10 @@ def test_host_validation_errors(lib):
     assert lib.mx_quantize_rowwise(None, 0, 32, 32, None, 32, None, 1, None) == 0
     assert lib.mx_quantize_colwise(P, 64, 20, 24, None, 0, P, 64, 64, P, 2, None, None) == 2
     assert lib.mx_quantize_colwise(P, 64, 32, 32, None, 0, P, 64, 32, P, 1, None, None) == 2
+    # with offsets the capacity must hold the padded total's bound M + 31*E (64 + 124)
+    assert lib.mx_quantize_colwise(P, 64, 32, 32, P, 4, P, 160, 160, P, 16, P, None) == 2
+    assert lib.mx_quantize_dual(P, 64, 32, 32, P, 4, P, 32, P, 16, P, 160, 160, P, 16, P, None) == 2
+    assert lib.mx_quantize_dual(P, 64, 32, 32, None, 0, P, 32, P, 16, P, 32, 32, P, 16, P, None) == 2
     assert lib.mx_gemm(P, P, 32, 1, P, P, 32, 1, 4, 4, 33, P, 4, 0, 0, None) == 2
     assert lib.mx_gemm(P, P, 32, 1, P, P, 32, 1, 4, 4, 32, P, 4, 2, 0, None) == 4  # out dtype
     assert lib.mx_gemm(P, P, 32, 1, P, P, 32, 1, 4, 4, 32, P, 4, 0, 7, None) == 4  # accum
@@ -67,7 +91,8 @@ def test_host_validation_errors(lib):
     assert lib.mxq_validate_offsets(None, 4, 10, None) == 1
 
 
-def test_per_group_validation_errors(lib):
+def test_per_group_validation_errors(host_only_lib):
+    lib = host_only_lib
     P = 4096
     # fp8_quantize_per_group(x, M, K, ldx, offsets, E, q, ldq, scales, ws, ws_bytes, stream)
     ws = lib.mxq_workspace_size(1, 64, 4, 0, 0)
@@ -88,10 +113,11 @@ def test_per_group_validation_errors(lib):
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 0, 8, 8, 32, P, 8, 0, 0, None) == 2
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 250, P, 4, 8, 8, 32, P, 8, 0, 0, None) == 3
     assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 40, P, 8, 0, 0, None) == 2
-    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 32, P, 8, 0, 1, None) == 4
+    assert lib.fp8_grouped_gemm_per_group(P, P, 32, P, P, 32, 256, P, 4, 8, 8, 32, P, 8, 0, 2, None) == 4
 
 
-def test_per_group_transposed_and_wgrad_validation_errors(lib):
+def test_per_group_transposed_and_wgrad_validation_errors(host_only_lib):
+    lib = host_only_lib
     P = 4096
     ws = lib.mxq_workspace_size(1, 64, 4, 0, 0)
     # fp8_quantize_per_group_colwise(x, M, K, ldx, offsets, E, qT, ldqT, M_cap, scales,
@@ -104,16 +130,18 @@ def test_per_group_transposed_and_wgrad_validation_errors(lib):
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 264, 256, P, P, P, ws, None) == 3
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, None, 4, P, 256, 256, P, P, P, ws, None) == 1
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 256, 256, P, P, P, ws - 4, None) == 5
+    assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 160, 160, P, P, P, ws, None) == 2
     # fp8_grouped_gemm_wgrad_per_group(at, sa, lda_t, bt, sb, ldb_t, poff, E, N, K, c, ldc,
     #                                  out, accum, stream)
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 40, P, P, 32, P, 2, 8, 8, P, 8, 0, 0, None) == 3
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, None, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 0, None) == 1
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 0, 8, 8, P, 8, 0, 0, None) == 2
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 4, 0, 0, None) == 2
-    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 1, None) == 4
+    assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 32, P, P, 32, P, 2, 8, 8, P, 8, 0, 2, None) == 4
 
 
-def test_size_limits_rejected(lib):
+def test_size_limits_rejected(host_only_lib):
+    lib = host_only_lib
     """Sizes past what the kernels index with 32-bit offsets are rejected on
     the host (no launch): a 256-row GEMM tile must span < 2^31 bytes, the
     row quantizer's segment count must fit 31 bits."""
@@ -133,7 +161,8 @@ def test_size_limits_rejected(lib):
     assert lib.mx_gemm(P + 2, P, ok_ld, 64, P, P, 32, 1, 4, 4, 32, P, 4, 0, 0, None) == 3
 
 
-def test_swiglu_product_validation_errors(lib):
+def test_swiglu_product_validation_errors(host_only_lib):
+    lib = host_only_lib
     P = 4096
     f = lib.mx_grouped_gemm_swiglu
 
@@ -152,6 +181,7 @@ def test_swiglu_product_validation_errors(lib):
     assert call(F=40, ldhq=64) == 2                     # F % 32
     assert call(K=40) == 2                              # K % 32
     assert call(cap=250) == 2                           # M_cap % 32
+    assert call(cap=160, ldhqT=160) == 2                # M_cap < M + 31 E
     assert call(off=None) == 1
     assert call(E=0) == 2
     assert call(E=257) == 2
@@ -171,7 +201,8 @@ def test_swiglu_product_validation_errors(lib):
     assert call(F=0) == 0                               # no-op
 
 
-def test_fused_per_group_and_blockwise_validation_errors(lib):
+def test_fused_per_group_and_blockwise_validation_errors(host_only_lib):
+    lib = host_only_lib
     P = 4096
     # fp8_grouped_gemm_per_group_swiglu(a, sa, lda, b, sb, ldb, b_estride, offsets, E, M, F, K,
     #                                   gu, ldgu, h, ldh, h_amax, stream)
@@ -201,6 +232,7 @@ def test_fused_per_group_and_blockwise_validation_errors(lib):
     assert d(P, 64, 32, 32, P, 4, None, P, 32, P, 256, 256, P, P, P, ws, None) == 5    # row maxima
     assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 256, P, P, P, ws - 4, None) == 5   # amax given
     assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 250, P, P, P, ws, None) == 2       # M_cap
+    assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 160, 160, P, P, P, ws, None) == 2       # < M + 31 E
     assert d(P, 64, 32, 32, P, 4, P, P, 32, P, 256, 256, None, P, P, ws, None) == 1    # scales
     # blockwise: fp8_quantize_blockwise_act(x, M, K, ldx, q, ldq, scales, lds, s)
     assert lib.fp8_quantize_blockwise_act(P, 8, 96, 96, P, 96, P, 1, None) == 2          # K % 128
@@ -216,4 +248,6 @@ def test_fused_per_group_and_blockwise_validation_errors(lib):
     assert h(P, P, 128, 0, P, P, 128, 1, 4, 4, 128, P, 4, 0, 0, None) == 2               # ldsa
     assert h(P, None, 128, 1, P, P, 128, 1, 4, 4, 128, P, 4, 0, 0, None) == 1
     assert h(P, P, 128, 1, P, P, 128, 1, 4, 4, 128, P, 4, 0, 3, None) == 4               # accum
+    # the blockwise GEMM has only the FP8 matrix-unit accumulation
+    assert h(P, P, 128, 1, P, P, 128, 1, 4, 4, 128, P, 4, 0, 1, None) == 4
     assert h(P, P, 128, 1, P, P, 128, 1, 0, 4, 128, None, 4, 0, 0, None) == 0            # M = 0
