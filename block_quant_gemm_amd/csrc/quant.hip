@@ -2,8 +2,8 @@
 // for gfx950, with their C-ABI launchers.
 //
 // Method: "DeepSeek-V3 16B FSDP2 MXFP8/HiF8 训练设计" §3 table (1x32 and 32x1
-// blocks, E8M0 scale from the current block) and §3.2 (current scaling,
-// scale = valid(amax) ? amax / format_max : 1.0 in FP32); "低精度训练特性
+// blocks, E8M0 scale from the current block) and §3.2 (current scaling: an
+// FP32 scale of amax / 448 for a finite non-zero amax, otherwise 1); "低精度训练特性
 // （MXFP8 / HiFloat8）" (block size 32; grouped quant for the expert wgrad);
 // E4M3 layout from "Transformer 与 LLM（06）：浮点格式、数值稳定性与混合精度" §二.2.
 //

@@ -141,9 +141,9 @@ MXQ_API int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ld
                      int64_t* offsets_padded, hipStream_t stream);
 
 /*
- * Per-tensor current-scaling FP8 E4M3 ([HP329] §3.2 current scaling,
- * "scale = valid(amax) ? amax / format_max : 1.0", FP32 scale; [FPBLOG] §七.2
- * first pass finds amax, second pass quantizes).
+ * Per-tensor current-scaling FP8 E4M3 ([HP329] §3.2 current scaling: FP32
+ * scale s = amax / 448 when amax is finite and non-zero, else s = 1;
+ * [FPBLOG] §七.2 first pass finds amax, second pass quantizes).
  *   x         : device, BF16 [n], contiguous, 16-byte aligned.
  *   q         : device, E4M3 [n], 16-byte aligned.
  *   scale     : device float[1] receiving s.
@@ -261,8 +261,20 @@ MXQ_API int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t K,
  *     each run of 8 consecutive-k products after aligning them to the largest
  *     exponent sum in the run, keeping 13 bits below it (smaller products are
  *     truncated toward zero), then adds the run sums in FP32.
- *  MXQ_ACC_FP32 : every product exact, summed in FP32.  Reserved: no kernel
- *     implements it yet, and every GEMM entry point returns MXQ_ERR_ARG for it.
+ *     Fast; outside the contract's |C - Y| <= 1e-5*S + 1e-6 when a run mixes
+ *     a large product with much smaller ones (outlier-heavy activations).
+ *  MXQ_ACC_FP32 : every product exact, summed in FP32 ("Transformer 与 LLM
+ *     （06）" §五.1: FP8 inputs, FP32 accumulation).  Each 32-block of codes is
+ *     widened to BF16 with its E8M0 scale folded in (v_cvt_scalef32_pk_bf16_fp8:
+ *     exact for scale codes 3..246, i.e. every block of finite BF16 values
+ *     whose largest magnitude is at least 2^-116; smaller blocks may lose
+ *     bits below 2^-133) and multiplied on the BF16 matrix instruction, whose
+ *     products are exact and whose sums stay within FP32 accuracy (measured
+ *     error <= 1e-6 S at K = 2048).  Meets the contract's rule; at most half
+ *     the FP8 mode's throughput (BF16 matrix peak).  Accepted by mx_gemm,
+ *     fp8_gemm_per_tensor, mx_grouped_gemm, mx_grouped_gemm_wgrad and the
+ *     per-group-scaled grouped GEMMs; fp8_gemm_blockwise returns MXQ_ERR_ARG
+ *     for it (that recipe promotes per block on the FP8 unit by design).
  */
 typedef enum { MXQ_ACC_MFMA_FP8 = 0, MXQ_ACC_FP32 = 1 } mxq_accum;
 
@@ -329,7 +341,7 @@ MXQ_API int fp8_quantize_blockwise_weight(const uint16_t* w, int64_t N, int64_t 
  *                 from fp8_quantize_blockwise_weight.
  *   c           : device [M, N] BF16 or FP32, row stride ldc.
  * Requires K % 128 == 0, lda/ldb multiples of 16 with 16-byte aligned codes,
- * 4-byte aligned scales.
+ * 4-byte aligned scales; accum == MXQ_ACC_MFMA_FP8 (else MXQ_ERR_ARG).
  */
 MXQ_API int fp8_gemm_blockwise(const uint8_t* a, const float* a_scales, int64_t lda, int64_t ldsa,
                        const uint8_t* b, const float* b_scales, int64_t ldb, int64_t ldsb,

@@ -11,8 +11,9 @@ Sources (cited by page title and section):
 
 * [HP329] "DeepSeek-V3 16B FSDP2 MXFP8/HiF8 训练设计" (mindspore/hyper-parallel
   issue #329): §3 format table (E4M3 data, E8M0 scale, 1x32/32x1 blocks,
-  scale from the current input), §3.2 (current scaling
-  ``scale = valid(amax) ? amax / format_max : 1.0`` in FP32), §8 direction
+  scale from the current input), §3.2 (current scaling: the FP32 scale is
+  the tensor's amax over the format's largest value when amax is finite and
+  non-zero, and 1 otherwise), §8 direction
   table, §13.4 matmul / grouped-matmul interface.
 * [FPBLOG] "Transformer 与 LLM（06）：浮点格式、数值稳定性与混合精度":
   §二.1 bit fields and the general value formula, §二.2 format table and the

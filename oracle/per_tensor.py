@@ -1,8 +1,8 @@
 """Per-tensor current-scaling FP8 (E4M3) oracle.  Test infrastructure.
 
-[HP329] §3.2: the current-scaling recipe takes ``scale = valid(amax) ?
-amax / format_max : 1.0``, held in FP32 and recomputed from the current tensor
-each call.  [FPBLOG] §七.2: per-tensor scaling shares one scale over the whole
+[HP329] §3.2: the current-scaling recipe divides the tensor's amax by the
+format's largest value when that amax is usable, and uses 1 otherwise; the
+scale is held in FP32 and recomputed from the current tensor each call.  [FPBLOG] §七.2: per-tensor scaling shares one scale over the whole
 tensor, found by a first pass over it (amax), then a second pass quantizes.
 
 Readings: format_max is E4M3's 448; "valid" means finite and > 0; amax is
@@ -50,8 +50,8 @@ def pg_quantize(x_bf16_bits, offsets):
 
     [HP329] §3 (format table: HiF8 current scaling keeps one FP32 scale per
     dense tensor and, for grouped tensors, one per leading group) and §3.2
-    (``scale = valid(amax) ? amax / format_max : 1.0``; 3-D grouped weights
-    use a per-leading-group scale); [TTNPU] MoE expert layers (each expert
+    (the scale rule above; 3-D grouped weights use a per-leading-group
+    scale); [TTNPU] MoE expert layers (each expert
     group shares one scale).  Reading: the groups of a [M, K] activation are
     its expert row ranges; a 3-D weight [E, N, K] is the same with offsets
     e * N; an empty group gets 1.0.

@@ -91,8 +91,8 @@ def _groups(counts):
 
 def test_per_group_scales_closed_form_and_empty_groups():
     """Each group's scale is its own amax / 448 (hand-picked amaxes whose
-    quotients are exact), an empty group gets 1.0 ([HP329] §3.2 'valid(amax)
-    ? amax / format_max : 1.0')."""
+    quotients are exact), an empty group gets 1.0 ([HP329] §3.2: a scale of 1
+    when there is no usable amax)."""
     offs = _groups([2, 0, 3, 1])
     x = bf16([[1.0, -3.5], [0.5, 2.0],                  # group 0: amax 3.5
               [-896.0, 1.0], [7.0, 0.0], [0.25, 448.0],  # group 2: amax 896
