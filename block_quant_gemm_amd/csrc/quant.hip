@@ -15,6 +15,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace mxq {
 
@@ -876,19 +877,29 @@ static int pg_scales(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   return launch_status();
 }
 
-static int quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                              const int64_t* offsets, int32_t E, const float* amax, uint8_t* q,
-                              int64_t ldq, float* scales, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+// Arguments of the row-major per-group quantization (workspace aside).
+static int per_group_args(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                          const int64_t* offsets, int32_t E, const uint8_t* q, int64_t ldq,
+                          const float* scales) {
   if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kPgMaxGroups) return MXQ_ERR_SHAPE;
-  if (!offsets || !scales || !workspace) return MXQ_ERR_NULL;
+  if (!offsets || !scales) return MXQ_ERR_NULL;
   if (M > 0 && K > 0 && (!x || !q)) return MXQ_ERR_NULL;
   if (K % 8 != 0) return MXQ_ERR_SHAPE;
   if (M > 0 && K > 0) {                              // strides of empty inputs are not used
     if (ldx < K || ldq < K) return MXQ_ERR_SHAPE;
     if (ldx % 8 != 0 || ldq % 8 != 0 || !aligned(x, 16) || !aligned(q, 8)) return MXQ_ERR_ALIGN;
   }
+  return MXQ_OK;
+}
+
+static int quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                              const int64_t* offsets, int32_t E, const float* amax, uint8_t* q,
+                              int64_t ldq, float* scales, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const int a = per_group_args(x, M, K, ldx, offsets, E, q, ldq, scales);
+  if (a != MXQ_OK) return a;
+  if (!workspace) return MXQ_ERR_NULL;
   if (!aligned(workspace, 4)) return MXQ_ERR_ALIGN;
   const int64_t ws_rows = amax ? 0 : M;              // row maxima only without amaxes
   if (workspace_bytes < mxq_workspace_size(MXQ_WS_PER_GROUP, ws_rows, E, 0, 0))
@@ -912,6 +923,53 @@ extern "C" int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, i
                                       size_t workspace_bytes, hipStream_t stream) {
   return quantize_per_group(x, M, K, ldx, offsets, E, nullptr, q, ldq, scales, workspace,
                             workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free per-group quantization.  The row maxima and group maxima
+// that fp8_quantize_per_group keeps in the caller's workspace live in this
+// file-scope device array instead: one copy per GPU, held until the process
+// ends, shared by every call on that GPU (calls that overlap on one GPU race).
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// its device address is looked up once per device and only that is used.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchWords = 1 << 18;          // 1 MiB: M + E <= 262144
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static uint32_t* g_scratch_ptr[kMaxDevices];        // device address of `scratch` per device
+
+// Device address of the current device's `scratch`, looked up on its first
+// use on that device (with it current) and kept.
+static int current_scratch(uint32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXQ_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MXQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXQ_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MXQ_OK;
+}
+
+extern "C" int fp8_quantize_per_group_noalloc(const uint16_t* x, int64_t M, int64_t K,
+                                              int64_t ldx, const int64_t* offsets, int32_t E,
+                                              uint8_t* q, int64_t ldq, float* scales,
+                                              hipStream_t stream) {
+  const int a = per_group_args(x, M, K, ldx, offsets, E, q, ldq, scales);
+  if (a != MXQ_OK) return a;
+  // row maxima [M] then group maxima [E]; every word read is written earlier
+  // in the same call, so nothing needs clearing between calls
+  if (M + E > kScratchWords) return MXQ_ERR_SHAPE;
+  uint32_t* ws = nullptr;
+  const int st = current_scratch(&ws);
+  if (st != MXQ_OK) return st;
+  return quantize_per_group(x, M, K, ldx, offsets, E, nullptr, q, ldq, scales, ws,
+                            (size_t)kScratchWords * sizeof(uint32_t), stream);
 }
 
 extern "C" int fp8_quantize_per_group_amax(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

@@ -32,6 +32,8 @@ _SIGS = {
     "fp8_quantize_per_tensor": (ctypes.c_int, [_p, _i64, _p, _p, _p, _sz, _p]),
     "fp8_quantize_per_group": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p,
                                               _p, _sz, _p]),
+    "fp8_quantize_per_group_noalloc": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p,
+                                                      _i64, _p, _p]),
     "mx_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _i64,
                                _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
     "fp8_gemm_per_tensor": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
@@ -245,6 +247,17 @@ def fp8_quantize_per_group(x, offsets, q=None, scales=None, workspace=None):
     _check(load().fp8_quantize_per_group(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q),
                                          q.stride(0), _ptr(scales), _ptr(workspace),
                                          workspace.numel(), _stream()))
+    return q, scales
+
+
+def fp8_quantize_per_group_noalloc(x, offsets, q, scales):
+    """fp8_quantize_per_group with the library's own per-GPU scratch instead of
+    a workspace: q uint8 [M, K] and scales float32 [E] are the caller's."""
+    x = _bf16_bits(x)
+    M, K = x.shape
+    E = offsets.numel() - 1
+    _check(load().fp8_quantize_per_group_noalloc(_ptr(x), M, K, x.stride(0), _ptr(offsets), E,
+                                                 _ptr(q), q.stride(0), _ptr(scales), _stream()))
     return q, scales
 
 

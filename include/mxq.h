@@ -183,6 +183,22 @@ MXQ_API int fp8_quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int6
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fp8_quantize_per_group for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument and no allocation.  The row and group
+ * maxima go to a 1 MiB device array inside the library, one per GPU, held
+ * until the process ends; its address is looked up on the first call on each
+ * device (the current device must be the stream's).  Limit: M + E <= 262144
+ * (MXQ_ERR_SHAPE beyond).  Calls that overlap on one GPU (concurrent streams
+ * or host threads) share that array and race; serialize them.
+ *   x, M, K, ldx, offsets, E, q, ldq, scales : as fp8_quantize_per_group,
+ *   with the same results bit for bit.
+ */
+MXQ_API int fp8_quantize_per_group_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   const int64_t* offsets, int32_t E,
+                                   uint8_t* q, int64_t ldq, float* scales, hipStream_t stream);
+
+/*
  * Transposed copy of the per-group current-scaling quantization, for the
  * products that contract over x's rows: the weight gradient over each
  * expert's tokens, the data gradient over a weight's output rows.  [HP329]

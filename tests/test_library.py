@@ -131,6 +131,14 @@ def test_per_group_transposed_and_wgrad_validation_errors(host_only_lib):
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, None, 4, P, 256, 256, P, P, P, ws, None) == 1
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 256, 256, P, P, P, ws - 4, None) == 5
     assert lib.fp8_quantize_per_group_colwise(P, 64, 32, 32, P, 4, P, 160, 160, P, P, P, ws, None) == 2
+    # fp8_quantize_per_group_noalloc(x, M, K, ldx, offsets, E, q, ldq, scales, stream):
+    # its scratch holds M + E <= 262144 words
+    nf = lib.fp8_quantize_per_group_noalloc
+    assert nf(P, 262144, 32, 32, P, 1, P, 32, P, None) == 2
+    assert nf(P, 262000, 32, 32, P, 256, P, 32, P, None) == 2
+    assert nf(P, 64, 32, 32, P, 0, P, 32, P, None) == 2
+    assert nf(P, -1, 32, 32, P, 4, P, 32, P, None) == 2
+    assert nf(P, 64, 32, 32, None, 4, P, 32, P, None) == 1
     # fp8_grouped_gemm_wgrad_per_group(at, sa, lda_t, bt, sb, ldb_t, poff, E, N, K, c, ldc,
     #                                  out, accum, stream)
     assert lib.fp8_grouped_gemm_wgrad_per_group(P, P, 40, P, P, 32, P, 2, 8, 8, P, 8, 0, 0, None) == 3
