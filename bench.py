@@ -292,6 +292,10 @@ def main():
     if not args.no_dense and not args.step_only:
         components["dense_ffn"] = dense_component(torch, mxq, workloads, to_dev, args.seed)
     if not args.step_only:
+        components["exact_accumulation"] = exact_mode(
+            torch, mxq, workloads, to_dev, args.seed, X, h, Wgu, Wdn, dY, dGU, offs_d,
+            w_off_gu, w_off_dn, flops, ms_step)
+    if not args.step_only:
         components["per_expert_scaling_step"] = per_expert_step(
             torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops)
         components["fused_swiglu_producer"] = fused_producer(
@@ -455,6 +459,90 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "relative_output_error_vs_fp32_of_bf16_inputs": errs,
         "vendor_hipblaslt_per_tensor_fp8": vendor,
     }
+
+
+def exact_mode(torch, mxq, workloads, to_dev, seed, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu,
+               w_off_dn, flops, fp8_ms):
+    """The exact-product accumulation (MXQ_ACC_FP32: E4M3 widened to BF16 with
+    the block scale folded in, on the BF16 matrix instruction), which meets
+    the contract's |C - Y| <= 1e-5 * S + 1e-6, against the FP8 matrix-unit
+    mode: the expert-layer step and the dense FFN forward GEMM in both modes,
+    and per configuration the fraction of FP8-mode outputs inside that
+    tolerance of the exact-mode output (FP32 outputs; S = |A|·|B|ᵀ from the
+    exact mode on the sign-cleared codes with the same scales).  The exact
+    mode's own distance from the FP64 product is pinned by the parity tests
+    (within the same rule), so this fraction stands in for the FP8 mode's
+    fraction inside the rule."""
+    ACC = mxq.ACC_FP32
+
+    def step():
+        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(X, offs_d)
+        wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(Wgu, w_off_gu)
+        mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                            ws.view(E, 2 * FFN, HIDDEN // 32), offs_d, accum=ACC)
+        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(h, offs_d)
+        dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(Wdn, w_off_dn)
+        mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
+                            offs_d, accum=ACC)
+        gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(dY, offs_d)
+        mxq.mx_grouped_gemm(gq, gs, *mxq.expert_view(dnT, dnTs, E, HIDDEN), offs_d, accum=ACC)
+        uq, us, duT, duTs, _ = mxq.mx_quantize_dual(dGU, offs_d)
+        mxq.mx_grouped_gemm(uq, us, *mxq.expert_view(guT, guTs, E, 2 * FFN), offs_d, accum=ACC)
+        mxq.mx_grouped_gemm_wgrad(dyT, dyTs, hT, hTs, poff, accum=ACC)
+        mxq.mx_grouped_gemm_wgrad(duT, duTs, xT, xTs, poff, accum=ACC)
+
+    _, ms = _timed(torch, step, reps=5)
+    out = {"step": {"ms_per_step": ms, "TFLOP_per_s_incl_quant": flops / (ms * 1e-3) / 1e12,
+                    "fp8_mode_ms_per_step": fp8_ms}}
+
+    mag = lambda q: q & 0x7F                          # |code|: the sign bit cleared
+
+    def agree(call, a, sa, b, sb):
+        c8 = call(a, sa, b, sb, mxq.ACC_MFMA_FP8)
+        cx = call(a, sa, b, sb, ACC)
+        sm = call(mag(a), sa, mag(b), sb, ACC)
+        ok = (c8 - cx).abs() <= 1e-5 * sm + 1e-6
+        fin = torch.isfinite(cx)
+        r = (ok & fin).sum().item() / max(1, fin.sum().item())
+        del c8, cx, sm, ok, fin
+        return r
+
+    fp32 = mxq.OUT_FP32
+    dense = lambda a, sa, b, sb, acc: mxq.mx_gemm(a, sa, b, sb, out_dtype=fp32, accum=acc)
+    grouped = lambda a, sa, b, sb, acc: mxq.mx_grouped_gemm(a, sa, b, sb, offs_d, out_dtype=fp32,
+                                                            accum=acc)
+    frac = {}
+    t = workloads.tiny_linear(seed)
+    frac["tiny_linear_256x256x512"] = agree(dense, *mxq.mx_quantize_rowwise(to_dev(t["A"])),
+                                            *mxq.mx_quantize_rowwise(to_dev(t["W"])))
+    d = workloads.dense_ffn(seed)
+    xq, xs = mxq.mx_quantize_rowwise(to_dev(d["X"]))
+    wq, ws = mxq.mx_quantize_rowwise(to_dev(d["W"]))
+    frac["dense_ffn_8192x10944x2048"] = agree(dense, xq, xs, wq, ws)
+    g8, tg8 = _timed(torch, lambda: mxq.mx_gemm(xq, xs, wq, ws))
+    gx, tgx = _timed(torch, lambda: mxq.mx_gemm(xq, xs, wq, ws, accum=ACC))
+    f2 = 2 * 8192 * 10944 * 2048
+    out["dense_ffn_gemm"] = {"exact_us": tgx * 1e3, "exact_TFLOP_per_s": f2 / (tgx * 1e-3) / 1e12,
+                             "fp8_us": tg8 * 1e3, "fp8_TFLOP_per_s": f2 / (tg8 * 1e-3) / 1e12}
+    del xq, xs, wq, ws, g8, gx
+    xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(X, offs_d)
+    wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(Wgu, w_off_gu)
+    hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(h, offs_d)
+    dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(Wdn, w_off_dn)
+    gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(dY, offs_d)
+    uq, us, duT, duTs, _ = mxq.mx_quantize_dual(dGU, offs_d)
+    frac["moe_gate_up_fwd"] = agree(grouped, xq, xs, wq.view(E, 2 * FFN, HIDDEN),
+                                    ws.view(E, 2 * FFN, HIDDEN // 32))
+    frac["moe_down_fwd"] = agree(grouped, hq, hs, dq.view(E, HIDDEN, FFN),
+                                 dsc.view(E, HIDDEN, FFN // 32))
+    frac["moe_down_dgrad"] = agree(grouped, gq, gs, *mxq.expert_view(dnT, dnTs, E, HIDDEN))
+    frac["moe_gate_up_dgrad"] = agree(grouped, uq, us, *mxq.expert_view(guT, guTs, E, 2 * FFN))
+    wg = lambda a, sa, b, sb, acc: mxq.mx_grouped_gemm_wgrad(a, sa, b, sb, poff, out_dtype=fp32,
+                                                             accum=acc)
+    frac["moe_down_wgrad"] = agree(wg, dyT, dyTs, hT, hTs)
+    frac["moe_gate_up_wgrad"] = agree(wg, duT, duTs, xT, xTs)
+    out["fp8_mode_fraction_inside_contract"] = frac
+    return out
 
 
 def per_expert_step(torch, mxq, X, h, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn, flops,
