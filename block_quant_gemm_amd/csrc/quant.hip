@@ -167,6 +167,11 @@ constexpr int kColLdsW = 34;     // LDS row stride of the input tile in dwords (
 constexpr int kColOutW = 144;    // LDS row stride of the staged codes in bytes (128 + 16 pad)
 constexpr int kColMaxGroupsLds = 256;
 constexpr int kColDualGroup = 4;  // column tiles per dispatch block (dual-axis)
+// Dual-axis: the row copy's codes and scales of kRowStage passes are staged in
+// LDS and leave as whole 128-byte row segments (and one scale dword per row)
+// rather than a 64-byte piece and two scale bytes per row and pass.
+constexpr int kRowStage = 2;
+constexpr int kRowStageW = kRowStage * kColTileK + 16;  // LDS row stride (bytes)
 
 // ROW (dual-axis quantization): the same pass also emits the row-wise (1x32)
 // codes and scales of every source row it holds.  Lane tid has 8 consecutive
@@ -186,6 +191,9 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   __shared__ uint32_t tile[kColTileM * kColLdsW];
   __shared__ __attribute__((aligned(16))) uint8_t outq[kColTileK * kColOutW];
   __shared__ __attribute__((aligned(16))) uint8_t outs[kColTileK * 4];
+  constexpr bool RSTAGE = ROW && !PG;
+  __shared__ __attribute__((aligned(16))) uint8_t rowq[RSTAGE ? kColTileM * kRowStageW : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t rowsc[RSTAGE ? kColTileM * 2 * kRowStage : 16];
   __shared__ int64_t s_off[kColMaxGroupsLds + 1];
   __shared__ int64_t s_poff[kColMaxGroupsLds + 1];
   __shared__ int64_t s_src0[4];
@@ -317,16 +325,16 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
       }
     } else if (ROW) {
       // Row-wise codes of the rows held in registers (every lane takes part
-      // in the quad exchanges; only valid rows and columns are stored).
+      // in the quad exchanges), staged for the flush below.
+      const int sp = pass % kRowStage;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         uint32_t lo, hi, code;
         quant8(cur[u], lo, hi, code);
-        const int64_t k = kb + chunk * 8;
-        if (rok[u] && k < K) {
-          store_stream(q + srow[u] * ldq + k, make_uint2(lo, hi));
-          if ((chunk & 3) == 0) sc[srow[u] * lds + (k >> 5)] = (uint8_t)code;
-        }
+        const int i = u * 32 + (tid >> 3);
+        *reinterpret_cast<uint2*>(&rowq[i * kRowStageW + sp * kColTileK + chunk * 8]) =
+            make_uint2(lo, hi);
+        if ((chunk & 3) == 0) rowsc[i * 2 * kRowStage + sp * 2 + (chunk >> 2)] = (uint8_t)code;
       }
     }
     __syncthreads();
@@ -416,6 +424,38 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
         for (int bb = 0; bb < 4; ++bb)
           if (p0 + 32 * bb < M_cap) d[bb] = (uint8_t)(sv >> (8 * bb));
       }
+    }
+    if (RSTAGE && (pass % kRowStage == kRowStage - 1 || pass + 1 == kColPasses ||
+                   kb + kColTileK >= K)) {
+      // Flush the staged passes: row segments of kRowStage * 64 bytes, 8 lanes
+      // x 16 B per row (valid rows and columns only), then the scales.
+      const int64_t k0 = kw0 + (int64_t)(pass - pass % kRowStage) * kColTileK;
+      constexpr int kLanesPerRow = kRowStage * kColTileK / 16;
+      constexpr int kRowsPerIt = 256 / kLanesPerRow;
+#pragma unroll
+      for (int it = 0; it < kColTileM / kRowsPerIt; ++it) {
+        const int row = it * kRowsPerIt + tid / kLanesPerRow, c16 = tid % kLanesPerRow;
+        const int b = row >> 5, r = row & 31;
+        const int64_t k = k0 + c16 * 16;
+        if (r < s_nvalid[b] && k < K)
+          store_stream(q + (s_src0[b] + r) * ldq + k,
+                       *reinterpret_cast<const uint4*>(&rowq[row * kRowStageW + c16 * 16]));
+      }
+      if (tid < kColTileM) {
+        const int b = tid >> 5, r = tid & 31;
+        if (r < s_nvalid[b]) {
+          uint8_t* d = sc + (s_src0[b] + r) * lds + (k0 >> 5);
+          const uint32_t sv = *reinterpret_cast<const uint32_t*>(&rowsc[tid * 2 * kRowStage]);
+          if (k0 + 32 * 2 * kRowStage <= K && (reinterpret_cast<uintptr_t>(d) & 3) == 0) {
+            *reinterpret_cast<uint32_t*>(d) = sv;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2 * kRowStage; ++j)
+              if (k0 + 32 * j < K) d[j] = (uint8_t)(sv >> (8 * j));
+          }
+        }
+      }
+      __syncthreads();                              // the next pass refills rowq
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
