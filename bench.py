@@ -43,8 +43,8 @@ KFN = {
     "q_row": "k_mx_rowwise",
     "q_col": "k_mx_colwise<false>",
     "q_dual": "k_mx_colwise<true>",
-    "gmm": "k_gemm<1,false,0,true>",
-    "wgrad": "k_gemm<2,false,0,true>",
+    "gmm": "k_gemm<1,false,0,true,false>",
+    "wgrad": "k_gemm<2,false,0,true,false>",
 }
 
 

@@ -8,6 +8,18 @@
 
 namespace mxq {
 
+// Size arithmetic of the host-side checks on caller-supplied (non-negative)
+// sizes: the product or sum, or INT64_MAX when it does not fit, so that a
+// limit check on the result rejects it instead of overflowing.
+inline int64_t sat_mul(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+inline int64_t sat_add(int64_t a, int64_t b) {
+  int64_t r;
+  return __builtin_add_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));

@@ -1199,8 +1199,13 @@ static int launch_gemm(GemmArgs& g, int64_t blocks, int out, int accum, hipStrea
   return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
+// Largest size or stride any GEMM accepts (2^39: far past any tensor that
+// fits in memory; it keeps tile counts and byte offsets of the checks in range).
+constexpr int64_t kMaxDim = int64_t(1) << 39;
+
 static int check_common(int64_t M, int64_t N, int64_t K, int64_t ldc, int out, int accum) {
   if (M < 0 || N < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || ldc > kMaxDim) return MXQ_ERR_SHAPE;
   if (out != MXQ_OUT_BF16 && out != MXQ_OUT_FP32) return MXQ_ERR_ARG;
   if (accum != MXQ_ACC_MFMA_FP8 && accum != MXQ_ACC_FP32) return MXQ_ERR_ARG;
   if (ldc < N) return MXQ_ERR_SHAPE;
@@ -1208,7 +1213,13 @@ static int check_common(int64_t M, int64_t N, int64_t K, int64_t ldc, int out, i
 }
 
 // Buffer offsets are 32-bit: one tile of rows must fit.
-static bool fits32(int64_t ld, int64_t K) { return ld * (TM + 1) + K < 0x7FFFFFFFLL; }
+static bool fits32(int64_t ld, int64_t K) {
+  return sat_add(sat_mul(ld, TM + 1), K) < 0x7FFFFFFFLL;
+}
+
+// Tiles of `n` rows (an upper bound for sizes near the int64 limit, which the
+// size checks reject anyway).
+static int64_t tiles_of(int64_t n, int64_t t) { return sat_add(n, t - 1) / t; }
 
 static int check_operand(const uint8_t* q, const void* s, int64_t ld, int64_t lds, int64_t K,
                          bool mx) {
@@ -1245,7 +1256,7 @@ extern "C" int mx_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t lda, in
     if ((st = check_operand(b, b_scale, ldb, ldsb, K, true))) return st;
   }
   GemmArgs g = make_args(a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, M, N, K, c, ldc);
-  return launch_gemm<kDense, false>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype, accum,
+  return launch_gemm<kDense, false>(g, sat_mul(tiles_of(M, TM), g.tiles_n), out_dtype, accum,
                                     stream);
 }
 
@@ -1264,7 +1275,7 @@ extern "C" int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64
   }
   GemmArgs g = make_args(a, nullptr, lda, 0, b, nullptr, ldb, 0, M, N, K, c, ldc);
   g.pta = a_scale; g.ptb = b_scale;
-  return launch_gemm<kDense, true>(g, ((M + TM - 1) / TM) * (int64_t)g.tiles_n, out_dtype, accum,
+  return launch_gemm<kDense, true>(g, sat_mul(tiles_of(M, TM), g.tiles_n), out_dtype, accum,
                                    stream);
 }
 
@@ -1283,13 +1294,14 @@ extern "C" int fp8_gemm_blockwise(const uint8_t* a, const float* a_scales, int64
     if ((st = check_operand(b, b_scales, ldb, 0, K, false))) return st;
     if (ldsa < K / 128 || ldsb < K / 128) return MXQ_ERR_SHAPE;
     // 32-bit scale offsets: a tile's 256 A rows and two B block rows
-    if (ldsa * 4 * (TM + 1) + K >= (1LL << 30) || ldsb * 4 * 3 + K >= (1LL << 30))
+    if (sat_add(sat_mul(ldsa, 4 * (TM + 1)), K) >= (1LL << 30) ||
+        sat_add(sat_mul(ldsb, 4 * 3), K) >= (1LL << 30))
       return MXQ_ERR_SHAPE;
   }
   if (accum != MXQ_ACC_MFMA_FP8) return MXQ_ERR_ARG;
   GemmArgs g = make_args(a, reinterpret_cast<const uint8_t*>(a_scales), lda, ldsa, b,
                          reinterpret_cast<const uint8_t*>(b_scales), ldb, ldsb, M, N, K, c, ldc);
-  const int64_t blocks = ((M + TM - 1) / TM) * (int64_t)g.tiles_n;
+  const int64_t blocks = sat_mul(tiles_of(M, TM), g.tiles_n);
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   g.nblocks = (uint32_t)blocks;
   if (out_dtype == MXQ_OUT_BF16)
@@ -1323,8 +1335,8 @@ extern "C" int mx_grouped_gemm(const uint8_t* a, const uint8_t* a_scale, int64_t
   GemmArgs g = make_args(a, a_scale, lda, ldsa, b, b_scale, ldb, ldsb, M, N, K, c, ldc);
   g.b_estride = b_estride; g.bs_estride = bs_estride;
   g.offsets = offsets; g.E = E;
-  const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
-  return launch_gemm<kVarM, false>(g, mtiles * (int64_t)g.tiles_n, out_dtype, accum, stream);
+  const int64_t mtiles = tiles_of(M, TM) + E;        // upper bound over all group splits
+  return launch_gemm<kVarM, false>(g, sat_mul(mtiles, g.tiles_n), out_dtype, accum, stream);
 }
 
 extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, int64_t lda,
@@ -1337,6 +1349,7 @@ extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, 
                                       int64_t M_cap, int64_t* offsets_padded,
                                       hipStream_t stream) {
   if (M < 0 || F < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
+  if (M > kMaxDim || F > kMaxDim || K > kMaxDim || M_cap > kMaxDim) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
   if (!offsets) return MXQ_ERR_NULL;
   if (F % 32 != 0 || K % 32 != 0 || M_cap % 32 != 0) return MXQ_ERR_SHAPE;
@@ -1354,7 +1367,8 @@ extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, 
   }
   if (b_estride < 0 || bs_estride < 0) return MXQ_ERR_SHAPE;
   // One descriptor spans an expert's 2F weight rows.
-  if (2 * F * ldb + K >= (1LL << 30) || 2 * F * ldsb + K / 32 + 16 >= (1LL << 30))
+  if (sat_add(sat_mul(2 * F, ldb), K) >= (1LL << 30) ||
+      sat_add(sat_mul(2 * F, ldsb), K / 32 + 16) >= (1LL << 30))
     return MXQ_ERR_SHAPE;
   if (b_estride % 16 != 0 || ldhq % 16 != 0 || ldhqT % 16 != 0 || !aligned(hq, 16) ||
       !aligned(hqT, 16))
@@ -1370,7 +1384,7 @@ extern "C" int mx_grouped_gemm_swiglu(const uint8_t* a, const uint8_t* a_scale, 
   g.poff = offsets_padded;
   // Every workgroup past the group tiles exits at once; with M == 0 the first
   // one still writes the padded offsets.
-  const int64_t blocks = ((M + TM - 1) / TM + E) * (int64_t)g.tiles_n;
+  const int64_t blocks = sat_mul(tiles_of(M, TM) + E, g.tiles_n);
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   g.nblocks = (uint32_t)blocks;
   if (ldsa % 16 == 0 && ldsb % 16 == 0)
@@ -1391,6 +1405,7 @@ extern "C" int fp8_grouped_gemm_per_group_swiglu(const uint8_t* a, const float* 
                                                  int64_t ldh, float* h_amax,
                                                  hipStream_t stream) {
   if (M < 0 || F < 0 || K < 0) return MXQ_ERR_SHAPE;
+  if (M > kMaxDim || F > kMaxDim || K > kMaxDim) return MXQ_ERR_SHAPE;
   if (E < 1 || E > kMaxGroups) return MXQ_ERR_SHAPE;
   if (!offsets || !a_scales || !b_scales || !h_amax) return MXQ_ERR_NULL;
   if (F % 32 != 0 || K % 32 != 0) return MXQ_ERR_SHAPE;
@@ -1402,7 +1417,7 @@ extern "C" int fp8_grouped_gemm_per_group_swiglu(const uint8_t* a, const float* 
     if ((st = check_operand(b, b_scales, ldb, 0, K, false))) return st;
   }
   if (b_estride < 0) return MXQ_ERR_SHAPE;
-  if (2 * F * ldb + K >= (1LL << 30)) return MXQ_ERR_SHAPE;
+  if (sat_add(sat_mul(2 * F, ldb), K) >= (1LL << 30)) return MXQ_ERR_SHAPE;
   if (b_estride % 16 != 0 || ldh % 8 != 0 || !aligned(h, 16)) return MXQ_ERR_ALIGN;
   if (gu && (ldgu % 8 != 0 || !aligned(gu, 16))) return MXQ_ERR_ALIGN;
   // every group's amax starts at zero (also for groups without rows)
@@ -1417,7 +1432,7 @@ extern "C" int fp8_grouped_gemm_per_group_swiglu(const uint8_t* a, const float* 
   g.F = F;
   g.h = h; g.ldh = ldh;
   g.hamax = reinterpret_cast<uint32_t*>(h_amax);
-  const int64_t blocks = ((M + TM - 1) / TM + E) * (int64_t)g.tiles_n;
+  const int64_t blocks = sat_mul(tiles_of(M, TM) + E, g.tiles_n);
   if (blocks > 0x7FFFFFFF) return MXQ_ERR_SHAPE;
   g.nblocks = (uint32_t)blocks;
   hipLaunchKernelGGL(k_gemm_swiglu_pg, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, g);
@@ -1446,8 +1461,8 @@ extern "C" int fp8_grouped_gemm_per_group(const uint8_t* a, const float* a_scale
   g.b_estride = b_estride;
   g.pta = a_scales; g.ptb = b_scales;
   g.offsets = offsets; g.E = E;
-  const int64_t mtiles = (M + TM - 1) / TM + E;      // upper bound over all group splits
-  return launch_gemm<kVarM, true>(g, mtiles * (int64_t)g.tiles_n, out_dtype, accum, stream);
+  const int64_t mtiles = tiles_of(M, TM) + E;        // upper bound over all group splits
+  return launch_gemm<kVarM, true>(g, sat_mul(mtiles, g.tiles_n), out_dtype, accum, stream);
 }
 
 extern "C" int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* a_scales,
@@ -1469,7 +1484,7 @@ extern "C" int fp8_grouped_gemm_wgrad_per_group(const uint8_t* at, const float* 
   GemmArgs g = make_args(at, nullptr, lda_t, 0, bt, nullptr, ldb_t, 0, N, K, cap, c, ldc);
   g.pta = a_scales; g.ptb = b_scales;
   g.offsets = offsets_padded; g.E = E;
-  const int64_t blocks = (int64_t)E * ((N + TM - 1) / TM) * g.tiles_n;
+  const int64_t blocks = sat_mul(sat_mul(E, tiles_of(N, TM)), g.tiles_n);
   return launch_gemm<kVarK, true>(g, blocks, out_dtype, accum, stream);
 }
 
@@ -1497,6 +1512,6 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* at, const uint8_t* at_scale,
   GemmArgs g = make_args(at, at_scale, lda_t, ldsa_t, bt, bt_scale, ldb_t, ldsb_t, N, K, cap, c,
                          ldc);
   g.offsets = offsets_padded; g.E = E;
-  const int64_t blocks = (int64_t)E * ((N + TM - 1) / TM) * g.tiles_n;
+  const int64_t blocks = sat_mul(sat_mul(E, tiles_of(N, TM)), g.tiles_n);
   return launch_gemm<kVarK, false>(g, blocks, out_dtype, accum, stream);
 }

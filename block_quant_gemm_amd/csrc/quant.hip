@@ -813,9 +813,13 @@ extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int6
   if (ldx % 8 != 0 || ldq % 16 != 0 || !aligned(x, 16) || !aligned(q, 16)) return MXQ_ERR_ALIGN;
   // A contiguous matrix is one long row: segments then cross row ends.
   int64_t rows = M, cols = K;
-  if (ldx == K && ldq == K && lds == K / 32 && M * K <= 0xFFFFFFFFLL) { rows = 1; cols = M * K; }
+  if (ldx == K && ldq == K && lds == K / 32 && sat_mul(M, K) <= 0xFFFFFFFFLL) {
+    rows = 1;
+    cols = M * K;
+  }
+  if (cols > 0xFFFFFFFFLL) return MXQ_ERR_SHAPE;
   int64_t segs_per_row = (cols + 511) / 512;
-  int64_t total = rows * segs_per_row;
+  int64_t total = sat_mul(rows, segs_per_row);
   if (cols > 0xFFFFFFFFLL || total > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   int64_t waves = (total + kRowUnroll - 1) / kRowUnroll;
   int64_t blocks = (waves + 3) / 4;
@@ -834,7 +838,7 @@ extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int6
 // input needs nothing.
 static int64_t padded_capacity(int64_t M, int32_t E) {
   if (M <= 0) return 0;
-  return E > 0 ? M + 31LL * E : (M + 31) / 32 * 32;
+  return E > 0 ? sat_add(M, 31LL * E) : sat_add(M, 31) / 32 * 32;
 }
 
 extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -850,9 +854,9 @@ extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int6
     return MXQ_ERR_SHAPE;
   if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
     return MXQ_ERR_ALIGN;
-  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
-  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
+  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   dim3 grid((uint32_t)(gx * gy));
   hipLaunchKernelGGL(k_mx_colwise<false>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
                      qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, nullptr, 0, nullptr, 0);
@@ -877,9 +881,9 @@ extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t
   if (ldqT % 16 != 0 || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(qT, 16) ||
       (x && !aligned(x, 16)) || (q && !aligned(q, 16)))
     return MXQ_ERR_ALIGN;
-  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
-  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
+  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   dim3 grid((uint32_t)(gx * gy));
   hipLaunchKernelGGL(k_mx_colwise<true>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
                      qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, q, ldq, scale, lds);
@@ -888,8 +892,11 @@ extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t
 
 extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t a1, int64_t, int64_t) {
   if (op == MXQ_WS_PER_TENSOR) return n > 0 ? kPtBlocks * sizeof(uint32_t) : 0;
-  if (op == MXQ_WS_PER_GROUP)                        // n = rows, a1 = groups
-    return n >= 0 && a1 > 0 ? (size_t)(n + a1) * sizeof(uint32_t) : 0;
+  if (op == MXQ_WS_PER_GROUP && n >= 0 && a1 > 0) {   // n = rows, a1 = groups
+    const int64_t words = sat_add(n, a1);
+    return words > INT64_MAX / (int64_t)sizeof(uint32_t) ? SIZE_MAX
+                                                          : (size_t)words * sizeof(uint32_t);
+  }
   return 0;
 }
 
@@ -947,7 +954,7 @@ static int quantize_per_group(const uint16_t* x, int64_t M, int64_t K, int64_t l
   uint32_t* rowmax = static_cast<uint32_t*>(workspace);
   uint32_t* gmax = rowmax + ws_rows;
   const int64_t waves = (int64_t)num_cus() * 64;    // rows in flight: 16 wavefronts per CU
-  const int64_t rows_blocks = (M + 3) / 4;
+  const int64_t rows_blocks = sat_add(M, 3) / 4;
   const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
                                                              : waves / 4);
   int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
@@ -1004,7 +1011,7 @@ extern "C" int fp8_quantize_per_group_noalloc(const uint16_t* x, int64_t M, int6
   if (a != MXQ_OK) return a;
   // row maxima [M] then group maxima [E]; every word read is written earlier
   // in the same call, so nothing needs clearing between calls
-  if (M + E > kScratchWords) return MXQ_ERR_SHAPE;
+  if (sat_add(M, E) > kScratchWords) return MXQ_ERR_SHAPE;
   uint32_t* ws = nullptr;
   const int st = current_scratch(&ws);
   if (st != MXQ_OK) return st;
@@ -1044,14 +1051,14 @@ static int quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, i
   uint32_t* rowmax = static_cast<uint32_t*>(workspace);
   uint32_t* gmax = rowmax + ws_rows;
   const int64_t waves = (int64_t)num_cus() * 64;
-  const int64_t rows_blocks = (M + 3) / 4;
+  const int64_t rows_blocks = sat_add(M, 3) / 4;
   const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
                                                              : waves / 4);
   int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
-  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
-  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
+  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   hipLaunchKernelGGL((k_mx_colwise<false, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
                      x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded,
                      nullptr, 0, nullptr, 0, gmax, scales);
@@ -1104,14 +1111,14 @@ extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t
   uint32_t* rowmax = static_cast<uint32_t*>(workspace);
   uint32_t* gmax = rowmax + ws_rows;
   const int64_t waves = (int64_t)num_cus() * 64;
-  const int64_t rows_blocks = (M + 3) / 4;
+  const int64_t rows_blocks = sat_add(M, 3) / 4;
   const uint32_t blocks = (uint32_t)(rows_blocks < waves / 4 ? (rows_blocks > 0 ? rows_blocks : 1)
                                                              : waves / 4);
   int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
-  const int64_t gx = (M_cap + kColTileM - 1) / kColTileM;
-  const int64_t gy = (K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (gx * gy > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
+  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   hipLaunchKernelGGL((k_mx_colwise<true, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
                      x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded, q, ldq,
                      nullptr, 0, gmax, scales);
@@ -1155,9 +1162,13 @@ extern "C" int fp8_quantize_blockwise_act(const uint16_t* x, int64_t M, int64_t 
     return MXQ_ERR_ALIGN;
   // A contiguous matrix is one long row (blocks never cross row ends: K % 128 == 0).
   int64_t rows = M, cols = K;
-  if (ldx == K && ldq == K && lds == K / 128 && M * K <= 0xFFFFFFFFLL) { rows = 1; cols = M * K; }
+  if (ldx == K && ldq == K && lds == K / 128 && sat_mul(M, K) <= 0xFFFFFFFFLL) {
+    rows = 1;
+    cols = M * K;
+  }
+  if (cols > 0xFFFFFFFFLL) return MXQ_ERR_SHAPE;
   const int64_t segs_per_row = (cols + 511) / 512;
-  const int64_t total = rows * segs_per_row;
+  const int64_t total = sat_mul(rows, segs_per_row);
   if (cols > 0xFFFFFFFFLL || total > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   int64_t blocks = (total + 3) / 4;
   const int64_t cap = (int64_t)num_cus() * 16;
@@ -1178,7 +1189,7 @@ extern "C" int fp8_quantize_blockwise_weight(const uint16_t* w, int64_t N, int64
   if (ldw < K || ldq < K || lds < K / 128) return MXQ_ERR_SHAPE;
   if (ldw % 8 != 0 || ldq % 8 != 0 || !aligned(w, 16) || !aligned(q, 8) || !aligned(scales, 4))
     return MXQ_ERR_ALIGN;
-  const int64_t nblocks = ((N + 127) / 128) * (K / 128);
+  const int64_t nblocks = sat_mul(sat_add(N, 127) / 128, K / 128);
   if (nblocks > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
   hipLaunchKernelGGL(k_bw_weight, dim3((uint32_t)nblocks), dim3(256), 0, stream, w, N, ldw, q,
                      ldq, scales, lds, (uint32_t)(K / 128));
