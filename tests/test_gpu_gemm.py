@@ -38,6 +38,35 @@ def _check(c, Y, S, out, accum, extra=None, label=""):
     return accept(host(c), Y, S, out == mxq.OUT_FP32, accum == mxq.ACC_FP32, extra, label)
 
 
+# Poisoned, guarded outputs: the result is a view of a larger buffer filled with
+# a NaN sentinel, so an output element the kernel does not write fails the
+# comparison, and the bands past its last row and column must stay intact.
+_SENTINEL = {mxq.OUT_BF16: (torch.bfloat16, 0x7FA5), mxq.OUT_FP32: (torch.float32, 0x7FC0A5A5)}
+
+
+def _guarded(rows, cols, out, lead=None, pad_rows=3, pad_cols=24):
+    """(view [rows, cols] or [lead, rows//lead, cols], buffer): the view's row
+    stride is cols + pad_cols and pad_rows sentinel rows follow it."""
+    dt, bits = _SENTINEL[out]
+    ld = cols + pad_cols
+    buf = torch.empty((rows + pad_rows, ld), dtype=dt, device="cuda")
+    ib = torch.int16 if dt == torch.bfloat16 else torch.int32
+    buf.view(ib).fill_(bits if dt == torch.float32 else bits - 0x10000 * (bits >= 0x8000))
+    v = buf[:rows, :cols]
+    if lead is not None:
+        v = buf[:rows].view(lead, rows // lead, ld)[:, :, :cols]
+    return v, buf
+
+
+def _guard_intact(buf, rows, cols, out):
+    dt, bits = _SENTINEL[out]
+    ib = torch.int16 if dt == torch.bfloat16 else torch.int32
+    b = buf.view(ib)
+    want = bits if dt == torch.float32 else bits - 0x10000 * (bits >= 0x8000)
+    assert torch.all(b[:, cols:] == want), "write past the last column"
+    assert torch.all(b[rows:] == want), "write past the last row"
+
+
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("accum", ACCS)
 def test_tiny_linear_forward(out, accum):
@@ -46,9 +75,11 @@ def test_tiny_linear_forward(out, accum):
     d = workloads.tiny_linear(0)
     aq, asc, ah, ash = _quant_rows(d["A"])
     bq, bsc, bh, bsh = _quant_rows(d["W"])
-    c = mxq.mx_gemm(aq, asc, bq, bsc, out_dtype=out, accum=accum)
+    c, buf = _guarded(256, 256, out)
+    mxq.mx_gemm(aq, asc, bq, bsc, out_dtype=out, accum=accum, c=c)
     Y, S = gemm.gemm_ref(mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh))
     _check(c, Y, S, out, accum, lambda: fp8_mfma_truncation_bound(ah, ash, bh, bsh))
+    _guard_intact(buf, 256, 256, out)
 
 
 def _relayout_scales(s, layout):
@@ -85,9 +116,11 @@ def test_dense_ragged(M, N, K, out, layout, accum):
     aq, asc, ah, ash = _quant_rows(a)
     bq, bsc, bh, bsh = _quant_rows(b)
     asc, bsc = _relayout_scales(asc, layout), _relayout_scales(bsc, layout)
-    c = mxq.mx_gemm(aq, asc, bq, bsc, out_dtype=out, accum=accum)
+    c, buf = _guarded(M, N, out)
+    mxq.mx_gemm(aq, asc, bq, bsc, out_dtype=out, accum=accum, c=c)
     Y, S = gemm.gemm_ref(mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh))
     _check(c, Y, S, out, accum, lambda: fp8_mfma_truncation_bound(ah, ash, bh, bsh))
+    _guard_intact(buf, M, N, out)
 
 
 @pytest.mark.parametrize("accum", ACCS)
@@ -193,12 +226,14 @@ def test_per_tensor_gemm(out, accum):
     b = workloads.bf16_normal((96, 512), 0.02, seed=5, name="pb")
     qa, sa = _pt_quant(a)
     qb, sb = _pt_quant(b)
-    c = mxq.fp8_gemm_per_tensor(qa, sa, qb, sb, out_dtype=out, accum=accum)
+    c, buf = _guarded(160, 96, out)
+    mxq.fp8_gemm_per_tensor(qa, sa, qb, sb, out_dtype=out, accum=accum, c=c)
     A = per_tensor.pt_dequantize(host(qa), host(sa)[0])
     B = per_tensor.pt_dequantize(host(qb), host(sb)[0])
     Y, S = gemm.gemm_ref(A, B)
     _check(c, Y, S, out, accum,
            lambda: _pt_extra(host(qa), host(sa)[0], host(qb), host(sb)[0]))
+    _guard_intact(buf, 160, 96, out)
 
 
 @pytest.mark.parametrize("accum", ACCS)
@@ -261,11 +296,14 @@ def test_grouped_var_m(counts, N, K, out, layout, accum):
     aq, asc, ah, ash = _quant_rows(a)
     bq, bsc, bh, bsh = _quant_rows(w)                       # [E*N, K]
     asc, bsc = _relayout_scales(asc, layout), _relayout_scales(bsc, layout)
-    c = mxq.mx_grouped_gemm(aq, asc, bq.view(E, N, K), bsc.view(E, N, K // 32),
-                            to_dev(offs), out_dtype=out, accum=accum)
+    M = a.shape[0]
+    c, buf = _guarded(M, N, out)
+    mxq.mx_grouped_gemm(aq, asc, bq.view(E, N, K), bsc.view(E, N, K // 32),
+                        to_dev(offs), out_dtype=out, accum=accum, c=c)
     A, B = mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh)
     Y, S = gemm.grouped_gemm_ref(A, B.reshape(E, N, K), offs)
     _check(c, Y, S, out, accum, lambda: _grouped_extra(ah, ash, bh, bsh, offs, N))
+    _guard_intact(buf, M, N, out)
 
 
 @pytest.mark.parametrize("counts,R,K,M_cap_extra", [
@@ -297,13 +335,15 @@ def test_grouped_dgrad_on_weight_column_copies(counts, R, K, M_cap_extra, out, a
     assert np.array_equal(host(qT)[:, :E * R], rqT) and np.array_equal(host(sT)[:, :E * R // 32], rsT)
     bq, bs = mxq.expert_view(qT, sT, E, R)                   # [E, K, R]
     gq, gs, gh, gsh = _quant_rows(dy)
-    c = mxq.mx_grouped_gemm(gq, gs, bq, bs, to_dev(offs), out_dtype=out, accum=accum)
+    c, buf = _guarded(M, K, out)
+    mxq.mx_grouped_gemm(gq, gs, bq, bs, to_dev(offs), out_dtype=out, accum=accum, c=c)
     # oracle: expert e's B operand is rows of W_eᵀ, i.e. its column copy
     Bv = mx.mx_dequantize(rqT, rsT).reshape(K, E, R).transpose(1, 0, 2)   # [E, K, R]
     Y, S = gemm.grouped_gemm_ref(mx.mx_dequantize(gh, gsh), Bv, offs)
     bh = rqT.reshape(K, E, R).transpose(1, 0, 2).reshape(E * K, R)
     bsh = rsT.reshape(K, E, R // 32).transpose(1, 0, 2).reshape(E * K, R // 32)
     _check(c, Y, S, out, accum, lambda: _grouped_extra(gh, gsh, bh, bsh, offs, K))
+    _guard_intact(buf, M, K, out)
 
 
 @pytest.mark.parametrize("accum", ACCS)
@@ -352,7 +392,8 @@ def test_grouped_wgrad(counts, N, K, out, layout, accum):
     assert np.array_equal(ah[:, :Mp], ra) and np.array_equal(ash[:, :Mp // 32], rsa)
     assert np.array_equal(bh[:, :Mp], rb) and np.array_equal(bsh[:, :Mp // 32], rsb)
     dysT, xsT = _relayout_scales(dysT, layout), _relayout_scales(xsT, layout)
-    c = mxq.mx_grouped_gemm_wgrad(dyT, dysT, xT, xsT, poff, out_dtype=out, accum=accum)
+    c, buf = _guarded(E * N, K, out, lead=E)
+    mxq.mx_grouped_gemm_wgrad(dyT, dysT, xT, xsT, poff, out_dtype=out, accum=accum, c=c)
     A, B = mx.mx_dequantize(ah, ash), mx.mx_dequantize(bh, bsh)
     Y, S = gemm.grouped_wgrad_ref(A, B, ph)
 
@@ -365,6 +406,7 @@ def test_grouped_wgrad(counts, N, K, out, layout, accum):
                                                   bh[:, lo:hi], bsh[:, lo // 32:hi // 32])
         return Tb
     _check(c, Y, S, out, accum, extra)
+    _guard_intact(buf, E * N, K, out)
     for e in np.nonzero(counts == 0)[0]:
         assert torch.all(c[e] == 0)
 
