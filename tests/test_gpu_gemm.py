@@ -102,9 +102,12 @@ def _relayout_scales(s, layout):
     return v
 
 
+# Up to 128 tiles of 256 rows the dense GEMM runs on 128-row tiles; the last
+# two shapes (81 and 289 tiles of 256 rows) take the 128-row and the 256-row
+# path with a ragged last row and column of tiles.
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (200, 136, 96), (129, 257, 160), (64, 40, 1408),
                                    (3, 500, 2048), (300, 264, 1056), (300, 1024, 256),
-                                   (257, 1300, 96)])
+                                   (257, 1300, 96), (2050, 2100, 64), (4100, 4130, 96)])
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
 @pytest.mark.parametrize("accum", ACCS)
