@@ -67,24 +67,44 @@ __device__ __forceinline__ void quant8(uint4 v, uint32_t& lo, uint32_t& hi, uint
   hi = cvt2_e4m3_sat<true>(bf16_lo(v.w) * inv, bf16_hi(v.w) * inv, hi);
 }
 
-__global__ __launch_bounds__(256) void k_mx_rowwise(
-    const uint16_t* __restrict__ x, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ sc, int64_t lds, uint32_t K, uint32_t segs_per_row,
-    uint32_t total_segs) {
+// Up to kRowBatch matrices in one launch: item i owns the global segment
+// groups [first, first + ceil(total / kRowUnroll) * kRowUnroll), so a group of
+// kRowUnroll consecutive segments never straddles two items.
+constexpr int kRowBatch = MXQ_ROWWISE_BATCH_MAX;
+struct RowItem {
+  const uint16_t* x;
+  uint8_t* q;
+  uint8_t* sc;
+  int64_t ldx, ldq, lds;
+  uint32_t K, segs_per_row, total, first;
+};
+struct RowBatch {
+  RowItem it[kRowBatch];
+  uint32_t n, total;
+};
+
+__global__ __launch_bounds__(256) void k_mx_rowwise(RowBatch b) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
-  for (uint32_t s0 = wave * kRowUnroll; s0 < total_segs; s0 += nwave * kRowUnroll) {
+  for (uint32_t s0 = wave * kRowUnroll; s0 < b.total; s0 += nwave * kRowUnroll) {
+    // the item of this group (wave-uniform; items in order of first)
+    int i = 0;
+#pragma unroll
+    for (int k = 1; k < kRowBatch; ++k)
+      if ((uint32_t)k < b.n && s0 >= b.it[k].first) i = k;
+    const RowItem t = i == 0 ? b.it[0] : i == 1 ? b.it[1] : i == 2 ? b.it[2] : b.it[3];
+    static_assert(kRowBatch == 4, "item selection above");
     uint4 v[kRowUnroll];
     uint32_t row[kRowUnroll], col[kRowUnroll];
     bool ok[kRowUnroll];
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
-      uint32_t s = s0 + u;
-      row[u] = s / segs_per_row;                    // wave-uniform
-      col[u] = (s - row[u] * segs_per_row) * 512u + lane * 8u;
-      ok[u] = (s < total_segs) && (col[u] < K);
-      v[u] = ok[u] ? *reinterpret_cast<const uint4*>(x + (int64_t)row[u] * ldx + col[u])
+      uint32_t s = s0 - t.first + u;
+      row[u] = s / t.segs_per_row;                  // wave-uniform
+      col[u] = (s - row[u] * t.segs_per_row) * 512u + lane * 8u;
+      ok[u] = (s < t.total) && (col[u] < t.K);
+      v[u] = ok[u] ? *reinterpret_cast<const uint4*>(t.x + (int64_t)row[u] * t.ldx + col[u])
                    : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -92,8 +112,8 @@ __global__ __launch_bounds__(256) void k_mx_rowwise(
       uint32_t lo, hi, code;
       quant8(v[u], lo, hi, code);
       if (ok[u]) {
-        store_stream(q + (int64_t)row[u] * ldq + col[u], make_uint2(lo, hi));
-        if ((lane & 3u) == 0u) sc[(int64_t)row[u] * lds + (col[u] >> 5)] = (uint8_t)code;
+        store_stream(t.q + (int64_t)row[u] * t.ldq + col[u], make_uint2(lo, hi));
+        if ((lane & 3u) == 0u) t.sc[(int64_t)row[u] * t.lds + (col[u] >> 5)] = (uint8_t)code;
       }
     }
   }
@@ -803,9 +823,11 @@ static int num_cus() {
   return cus;
 }
 
-extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                   uint8_t* q, int64_t ldq, uint8_t* scale, int64_t lds,
-                                   hipStream_t stream) {
+// Checks one row-wise item and fills its segment range (first and total are
+// set by the caller).  Returns MXQ_OK with it->total == 0 for an empty item.
+static int rowwise_item(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                        int64_t ldq, uint8_t* scale, int64_t lds, RowItem* it) {
+  *it = RowItem{};
   if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
   if (M == 0 || K == 0) return MXQ_OK;
   if (!x || !q || !scale) return MXQ_ERR_NULL;
@@ -818,18 +840,67 @@ extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int6
     cols = M * K;
   }
   if (cols > 0xFFFFFFFFLL) return MXQ_ERR_SHAPE;
-  int64_t segs_per_row = (cols + 511) / 512;
-  int64_t total = sat_mul(rows, segs_per_row);
-  if (cols > 0xFFFFFFFFLL || total > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
-  int64_t waves = (total + kRowUnroll - 1) / kRowUnroll;
+  const int64_t segs_per_row = (cols + 511) / 512;
+  const int64_t total = sat_mul(rows, segs_per_row);
+  if (total > 0x7FFFFFFFLL - 2 * kRowUnroll) return MXQ_ERR_SHAPE;
+  it->x = x;
+  it->q = q;
+  it->sc = scale;
+  it->ldx = rows == 1 ? cols : ldx;
+  it->ldq = rows == 1 ? cols : ldq;
+  it->lds = rows == 1 ? cols / 32 : lds;
+  it->K = (uint32_t)cols;
+  it->segs_per_row = (uint32_t)segs_per_row;
+  it->total = (uint32_t)total;
+  return MXQ_OK;
+}
+
+static int launch_rowwise(RowBatch& b, hipStream_t stream) {
+  // pack the non-empty items, each starting on a group boundary
+  uint32_t n = 0;
+  int64_t first = 0;
+  for (uint32_t i = 0; i < b.n; ++i) {
+    if (b.it[i].total == 0) continue;
+    b.it[n] = b.it[i];
+    b.it[n].first = (uint32_t)first;
+    first += ((int64_t)b.it[i].total + kRowUnroll - 1) / kRowUnroll * kRowUnroll;
+    if (first > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+    ++n;
+  }
+  if (n == 0) return MXQ_OK;
+  b.n = n;
+  b.total = (uint32_t)first;
+  const int64_t waves = first / kRowUnroll;
   int64_t blocks = (waves + 3) / 4;
-  int64_t cap = (int64_t)num_cus() * 16;
+  const int64_t cap = (int64_t)num_cus() * 16;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(k_mx_rowwise, dim3((uint32_t)blocks), dim3(256), 0, stream, x,
-                     rows == 1 ? cols : ldx, q, rows == 1 ? cols : ldq, scale,
-                     rows == 1 ? cols / 32 : lds, (uint32_t)cols, (uint32_t)segs_per_row,
-                     (uint32_t)total);
+  hipLaunchKernelGGL(k_mx_rowwise, dim3((uint32_t)blocks), dim3(256), 0, stream, b);
   return launch_status();
+}
+
+extern "C" int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, uint8_t* scale, int64_t lds,
+                                   hipStream_t stream) {
+  RowBatch b{};
+  const int st = rowwise_item(x, M, K, ldx, q, ldq, scale, lds, &b.it[0]);
+  if (st != MXQ_OK) return st;
+  b.n = 1;
+  return launch_rowwise(b, stream);
+}
+
+extern "C" int mx_quantize_rowwise_batch(const mxq_rowwise_item* items, int32_t n,
+                                         hipStream_t stream) {
+  if (n < 1 || n > kRowBatch) return MXQ_ERR_SHAPE;
+  if (!items) return MXQ_ERR_NULL;
+  RowBatch b{};
+  for (int32_t i = 0; i < n; ++i) {
+    const mxq_rowwise_item& it = items[i];
+    const int st = rowwise_item(it.x, it.M, it.K, it.ldx, it.q, it.ldq, it.scale, it.lds,
+                                &b.it[i]);
+    if (st != MXQ_OK) return st;
+  }
+  b.n = (uint32_t)n;
+  return launch_rowwise(b, stream);
 }
 
 // Columns a grouped column copy may need: every group padded to a multiple

@@ -20,11 +20,20 @@ ACC_MFMA_FP8, ACC_FP32 = 0, 1
 WS_PER_TENSOR, WS_PER_GROUP = 0, 1
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+ROWWISE_BATCH_MAX = 4
+
+
+class RowwiseItem(ctypes.Structure):
+    """mxq_rowwise_item of mxq.h."""
+    _fields_ = [("x", _p), ("M", _i64), ("K", _i64), ("ldx", _i64), ("q", _p), ("ldq", _i64),
+                ("scale", _p), ("lds", _i64)]
+
 
 _SIGS = {
     "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mxq_version": (ctypes.c_int, []),
     "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "mx_quantize_rowwise_batch": (ctypes.c_int, [ctypes.POINTER(RowwiseItem), _i32, _p]),
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _i64,
                                            _p, _i64, _p, _p]),
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _i64,
@@ -147,6 +156,23 @@ def mx_quantize_rowwise(x, q=None, scale=None):
     _check(load().mx_quantize_rowwise(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0),
                                       _ptr(scale), scale.stride(0), _stream()))
     return q, scale
+
+
+def mx_quantize_rowwise_batch(xs):
+    """Row-wise MX quantization of several BF16 matrices in one launch (e.g. a
+    Linear's input and weight).  Returns [(codes, scales), ...] as
+    mx_quantize_rowwise would for each."""
+    xs = [_bf16_bits(x) for x in xs]
+    outs, items = [], (RowwiseItem * len(xs))()
+    for i, x in enumerate(xs):
+        M, K = x.shape
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        scale = _scale_buffer(M, K // 32, x.device)
+        items[i] = RowwiseItem(_ptr(x), M, K, x.stride(0), _ptr(q), q.stride(0), _ptr(scale),
+                               scale.stride(0))
+        outs.append((q, scale))
+    _check(load().mx_quantize_rowwise_batch(items, len(xs), _stream()))
+    return outs
 
 
 def colwise_capacity(M, E=None):

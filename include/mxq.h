@@ -88,6 +88,29 @@ MXQ_API int mx_quantize_rowwise(const uint16_t* x, int64_t M, int64_t K, int64_t
                         hipStream_t stream);
 
 /*
+ * Several row-wise MX quantizations in one launch, e.g. a Linear's input and
+ * weight, whose forward product reads both row copies ([HP329] §8 direction
+ * table).  Each item receives exactly the codes and scales that
+ * mx_quantize_rowwise gives it, under the same requirements; an item with
+ * M == 0 or K == 0 is skipped.
+ *   items : host array of n items, read during the call only.
+ *   n     : 1 .. MXQ_ROWWISE_BATCH_MAX (else MXQ_ERR_SHAPE).
+ * The first item that fails a check decides the returned status and nothing
+ * is launched.  Items must not write overlapping memory.
+ */
+#define MXQ_ROWWISE_BATCH_MAX 4
+typedef struct mxq_rowwise_item {
+  const uint16_t* x;    /* device, BF16 [M, K], row stride ldx elements */
+  int64_t M, K, ldx;
+  uint8_t* q;           /* device, E4M3 [M, K], row stride ldq bytes */
+  int64_t ldq;
+  uint8_t* scale;       /* device, E8M0 [M, K/32], row stride lds bytes */
+  int64_t lds;
+} mxq_rowwise_item;
+MXQ_API int mx_quantize_rowwise_batch(const mxq_rowwise_item* items, int32_t n,
+                                      hipStream_t stream);
+
+/*
  * Column-wise (32x1) MX quantization with transposed output ([HP329] §3 table
  * "32×1 block", §3.1 row and col copies are distinct physical data), in its
  * grouped form for the MoE wgrad operands ([TTNPU] "MoE 专家层低精度": the

@@ -51,6 +51,30 @@ int main() {
          MXQ_ERR_SHAPE);
   EXPECT(mx_quantize_rowwise(X, 1 << 20, 1 << 16, 1 << 16, P, 1 << 16, P, 1 << 11, nullptr),
          HIP);                                                // 2^36 elements, row by row
+  // ---- row-wise, several matrices in one launch ----
+  {
+    const mxq_rowwise_item good{X, 4, 32, 32, P, 32, P, 1};
+    const mxq_rowwise_item bad_k{X, 4, 40, 40, P, 48, P, 2};
+    const mxq_rowwise_item odd{X + 1, 4, 32, 32, P, 32, P, 1};
+    const mxq_rowwise_item empty{nullptr, 0, 32, 32, nullptr, 32, nullptr, 1};
+    const mxq_rowwise_item huge{X, HUGE_, 1 << 16, 1 << 16, P, 1 << 16, P, 1 << 11};
+    // 2^23 strided rows of 2^16: 2^30 segments each, so two pass 2^31 together
+    const mxq_rowwise_item half{X, INT64_C(1) << 23, 1 << 16, (1 << 16) + 8, P, 1 << 16, P,
+                                1 << 11};
+    const mxq_rowwise_item five[5] = {good, good, good, good, good};
+    EXPECT(mx_quantize_rowwise_batch(five, 0, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_rowwise_batch(five, 5, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_rowwise_batch(nullptr, 1, nullptr), MXQ_ERR_NULL);
+    const mxq_rowwise_item a[2] = {good, bad_k}, b2[2] = {odd, good}, c[2] = {empty, empty};
+    const mxq_rowwise_item d[2] = {good, huge}, e[2] = {half, half}, f[3] = {empty, half, good};
+    EXPECT(mx_quantize_rowwise_batch(a, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_rowwise_batch(b2, 2, nullptr), MXQ_ERR_ALIGN);
+    EXPECT(mx_quantize_rowwise_batch(c, 2, nullptr), MXQ_OK);   // nothing to launch
+    EXPECT(mx_quantize_rowwise_batch(d, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_rowwise_batch(e, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_rowwise_batch(f, 3, nullptr), HIP);
+    EXPECT(mx_quantize_rowwise_batch(five, 4, nullptr), HIP);
+  }
   // ---- column-wise / dual ----
   EXPECT(mx_quantize_colwise(X, 64, 20, 24, nullptr, 0, P, 64, 64, P, 2, nullptr, nullptr),
          MXQ_ERR_SHAPE);

@@ -95,6 +95,32 @@ def test_rowwise_empty_is_noop():
     assert q.shape == (0, 64) and s.shape == (0, 2)
 
 
+def test_rowwise_batch_equals_single_calls():
+    """One launch for several matrices: a Linear's input and weight (contiguous,
+    one long row each), a strided view (row by row, segment groups that end
+    mid-row), an empty item in between, and a matrix of one segment: every
+    item bit-equal to its own mx_quantize_rowwise call and to the oracle."""
+    say("rowwise batch: 4096x2048 input, 2048x2048 weight, strided 37x544, empty, 1x32")
+    a = workloads.bf16_normal((4096, 2048), 1.0, seed=1, name="rb_a", outlier_frac=0.01,
+                              outlier_scale=100.0)
+    w = workloads.bf16_normal((2048, 2048), 0.02, seed=2, name="rb_w")
+    big = workloads.bf16_normal((37, 544 + 40), 1.0, seed=3, name="rb_s")
+    one = workloads.bf16_normal((1, 32), 1.0, seed=4, name="rb_o")
+    xs = [to_dev_bf16(a), to_dev_bf16(w), to_dev_bf16(big)[:, :544],
+          torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), to_dev_bf16(one)]
+    hosts = [a, w, np.ascontiguousarray(big[:, :544]), None, one]
+    outs = mxq.mx_quantize_rowwise_batch(xs[:4])
+    outs += mxq.mx_quantize_rowwise_batch(xs[4:])
+    assert outs[3][0].shape == (0, 64)
+    for i, (x, xh, (q, s)) in enumerate(zip(xs, hosts, outs)):
+        if xh is None:
+            continue
+        q1, s1 = mxq.mx_quantize_rowwise(x)
+        assert torch.equal(q, q1) and torch.equal(s, s1), f"item {i} differs from its own call"
+        rc, rs = mx.mx_quantize_rowwise(xh)
+        assert np.array_equal(host(q), rc) and np.array_equal(host(s), rs), f"item {i} vs oracle"
+
+
 # ---------------------------------------------------------------------------
 # column-wise
 # ---------------------------------------------------------------------------

@@ -91,6 +91,27 @@ def test_host_validation_errors(host_only_lib):
     assert lib.mxq_validate_offsets(None, 4, 10, None) == 1
 
 
+def test_rowwise_batch_validation_errors(host_only_lib):
+    lib = host_only_lib
+    P = 4096
+    It = mxq.RowwiseItem
+
+    def call(*items, n=None):
+        arr = (It * len(items))(*items)
+        return lib.mx_quantize_rowwise_batch(arr, len(items) if n is None else n, None)
+
+    good = It(P, 4, 32, 32, P, 32, P, 1)
+    assert call(good, n=0) == 2                                     # n out of range
+    assert call(*[good] * 5) == 2                                   # past the batch maximum
+    assert lib.mx_quantize_rowwise_batch(None, 1, None) == 1        # NULL items
+    assert call(good, It(P, 4, 40, 40, P, 48, P, 2)) == 2           # K % 32 in item 1
+    assert call(It(None, 4, 32, 32, P, 32, P, 1), good) == 1        # NULL x in item 0
+    assert call(good, It(P + 2, 4, 32, 32, P, 32, P, 1)) == 3       # misaligned x in item 1
+    empty = It(None, 0, 32, 32, None, 32, None, 1)
+    assert call(empty, empty) == 0                                  # nothing to launch
+    assert mxq.ROWWISE_BATCH_MAX == 4
+
+
 def test_per_group_validation_errors(host_only_lib):
     lib = host_only_lib
     P = 4096
