@@ -73,6 +73,43 @@ def parse():
     return ap.parse_args()
 
 
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    skips the system-scope fence (a cache write-back and invalidation) that a
+    default event performs, which the kernel after it would otherwise pay.
+    Measured on the expert-layer step: events around the four variable-M
+    launches add 19 us per step with torch's (default) events, 7 us with
+    these.  Elapsed times are read after a device synchronization."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self, torch):
+        import ctypes
+        if HipEvent._hip is None:
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self.ctypes, self.torch = ctypes, torch
+        self.e = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.e),
+                                                  ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def record(self):
+        stream = self.ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if HipEvent._hip.hipEventRecord(self.e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = self.ctypes.c_float()
+        if HipEvent._hip.hipEventElapsedTime(self.ctypes.byref(ms), self.e, end.e) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.e:
+            HipEvent._hip.hipEventDestroy(self.e)
+
+
 class Timer:
     """Per-label HIP event pairs on the current stream."""
 
@@ -89,8 +126,7 @@ class Timer:
     def run(self, label, fn, *a, **k):
         if not self.on or (self.only is not None and label != self.only):
             return fn(*a, **k)
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
+        s, e = HipEvent(self.torch), HipEvent(self.torch)
         s.record()
         r = fn(*a, **k)
         e.record()
@@ -203,7 +239,7 @@ def main():
     torch.cuda.synchronize()
     # Breakdown pass (K steps, not the timed region): HIP events around every
     # launch give each kernel class's share of the step.  Each recorded event
-    # costs the stream a few microseconds, so the timed region below records
+    # still costs the stream a little, so the timed region below records
     # events around the roofline kernel's launches only.
     T.on = True
     for _ in range(args.steps):
