@@ -418,6 +418,92 @@ __device__ void group_table(const int64_t* offsets, int E, int64_t M, int64_t* s
   __syncthreads();
 }
 
+// Weight-gradient tile order: the experts by padded token count, largest
+// first, so the longest tiles start first whatever the routing's expert order.
+// Counts are ranked by binade (the bit length of count / 32, so within a
+// factor of 2), ties by index; experts already in that order keep it.
+// Wavefront 0 checks the order with one ballot per 64 experts, else ranks them
+// with one ballot per binade present.  s_off receives the offsets rounded down
+// to 32 and clamped to [0, cap] (as the tiles read them) and s_perm[r] the
+// expert of rank r; the ranks form a permutation whatever the offsets hold.
+__device__ void expert_order(const int64_t* offsets, int E, int64_t cap, int64_t* s_off,
+                             int32_t* s_perm) {
+  const int t = threadIdx.x;
+  for (int e = t; e <= E; e += blockDim.x) {
+    const int64_t o = offsets[e] & ~31LL;
+    s_off[e] = o < 0 ? 0 : (o > cap ? cap : o);
+  }
+  __syncthreads();
+  if (t < 64) {
+    constexpr int R = kMaxGroups / 64;              // rounds of 64 experts
+    const int rounds = (E + 63) / 64;
+    int bin[R];                                     // -1 past E
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int e = c * 64 + t;
+      int b = -1;
+      if (e < E) {
+        const int64_t d = s_off[e + 1] - s_off[e];
+        const uint64_t u = d > 0 ? (uint64_t)d >> 5 : 0;
+        b = u ? 64 - __builtin_clzll(u) : 0;
+      }
+      bin[c] = b;
+    }
+    // in order already: binades non-increasing with the index
+    bool sorted = true;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      if (c < rounds) {
+        int nxt = __shfl_down(bin[c], 1, 64);       // expert e + 1
+        const int first_next = c + 1 < R ? __shfl(bin[c + 1 < R ? c + 1 : c], 0, 64) : -1;
+        if (t == 63) nxt = first_next;              // lane 63: the next round's first
+        if (__ballot(bin[c] >= 0 && nxt > bin[c]) != 0) sorted = false;
+      }
+    }
+    if (sorted) {
+      for (int e = t; e < E; e += 64) s_perm[e] = e;
+    } else {
+      // rank = experts in higher binades + experts of the same binade with a
+      // lower index (earlier rounds, then lower lanes of this round), over the
+      // binades present only
+      int bhi = -1, blo = 64;
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if (bin[c] >= 0) {
+          bhi = bhi > bin[c] ? bhi : bin[c];
+          blo = blo < bin[c] ? blo : bin[c];
+        }
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) {
+        const int ohi = __shfl_xor(bhi, sh, 64), olo = __shfl_xor(blo, sh, 64);
+        bhi = bhi > ohi ? bhi : ohi;
+        blo = blo < olo ? blo : olo;
+      }
+      bhi = __builtin_amdgcn_readfirstlane(bhi);
+      blo = __builtin_amdgcn_readfirstlane(blo);
+      int above = 0, rank[R];
+#pragma unroll
+      for (int c = 0; c < R; ++c) rank[c] = 0;
+      for (int b = bhi; b >= blo; --b) {
+        int before = 0;
+#pragma unroll
+        for (int c = 0; c < R; ++c) {
+          if (c < rounds) {
+            const uint64_t m = __ballot(bin[c] == b);
+            if (bin[c] == b) rank[c] = above + before + __builtin_popcountll(m & ((1ull << t) - 1ull));
+            before += __builtin_popcountll(m);
+          }
+        }
+        above += before;
+      }
+#pragma unroll
+      for (int c = 0; c < R; ++c)
+        if (bin[c] >= 0) s_perm[rank[c]] = c * 64 + t;
+    }
+  }
+  __syncthreads();
+}
+
 // Vector-memory instructions a wavefront issues per stage: 4 + 4 tile loads,
 // plus 2 + 2 scale-byte loads for MX scales read byte by byte.
 template <bool SBYTES>
@@ -470,7 +556,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   __shared__ __attribute__((aligned(16)))
   uint32_t ssc[SBYTES ? kSlots * 2 * 2 * 2 * TM
                       : (SWIN ? kWinSlots * kWinBytes / 4 : (BLK ? kSlots * kBlkScaleWords : 1))];
-  __shared__ int64_t s_off[KIND == kVarM ? kMaxGroups + 1 : 1];
+  __shared__ int64_t s_off[KIND == kVarM || KIND == kVarK ? kMaxGroups + 1 : 1];
+  __shared__ int32_t s_perm[KIND == kVarK ? kMaxGroups : 1];
   __shared__ int32_t s_start[KIND == kVarM ? kMaxGroups + 1 : 1];
 
   const int t = threadIdx.x;
@@ -548,22 +635,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
   } else {
     // variable K: tile = (e, tm over rows of A = dW rows, tn over rows of B =
     // dW cols).  Work per tile is proportional to the group's tokens, so the
-    // dispatch stays in tile order for balance, except that within each block
-    // of 64 workgroups (8 per XCD, dispatched round-robin) workgroup
-    // 64q + 8r + x takes tile 64q + 8x + r: 8 consecutive tiles, which share
-    // an A panel, then run on one XCD and share its L2.
+    // experts go largest first (expert_order) and the dispatch follows that
+    // tile order, except that within each block of 64 workgroups (8 per XCD,
+    // dispatched round-robin) workgroup 64q + 8r + x takes tile 64q + 8x + r:
+    // 8 consecutive tiles, which share an A panel, then run on one XCD and
+    // share its L2.
     uint32_t tile = blockIdx.x;
     if ((tile | 63u) < g.nblocks) tile = (tile & ~63u) | ((tile & 7u) << 3) | ((tile >> 3) & 7u);
     const uint32_t tn = tile % g.tiles_n, tmg = tile / g.tiles_n;
     const uint32_t tiles_m = (uint32_t)((g.M + TM - 1) / TM);
-    const int e = (int)(tmg / tiles_m);
+    // g.K holds the token capacity; padded offsets are multiples of 32, and
+    // rounding down keeps every access inside [0, capacity) even for
+    // malformed offsets.
+    expert_order(g.offsets, g.E, g.K & ~31LL, s_off, s_perm);
+    const int e = __builtin_amdgcn_readfirstlane(s_perm[tmg / tiles_m]);
     m0 = (int64_t)(tmg % tiles_m) * TM;
     n0 = (int64_t)tn * TN;
-    // Padded offsets are multiples of 32; rounding down keeps every access
-    // inside [0, capacity) even for malformed offsets.
-    int64_t lo_t = g.offsets[e] & ~31LL, hi_t = g.offsets[e + 1] & ~31LL;
-    if (lo_t < 0) lo_t = 0;
-    if (hi_t > (g.K & ~31LL)) hi_t = g.K & ~31LL;     // g.K holds the token capacity
+    const int64_t lo_t = s_off[e], hi_t = s_off[e + 1];
     kdim = hi_t > lo_t ? hi_t - lo_t : 0;
     c_rows = g.M - m0;
     group = e;

@@ -373,6 +373,10 @@ def test_grouped_var_m_equals_dense_for_one_group(accum):
     ([700, 33, 1100, 0, 517], 288, 160),
     ([300, 0, 45, 513], 296, 768),
     ([300, 0, 45, 513], 264, 600),
+    # more experts than one wavefront ranks at once: unordered sizes with empty
+    # experts (ranked largest first), and sizes already in order (kept)
+    (np.random.default_rng(7).integers(0, 40, 130).tolist(), 64, 64),
+    (sorted(np.random.default_rng(8).integers(0, 90, 100).tolist(), reverse=True), 72, 96),
 ])
 @pytest.mark.parametrize("out", OUTS)
 @pytest.mark.parametrize("layout", ["pad16", "odd", "shift5"])
