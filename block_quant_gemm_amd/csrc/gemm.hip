@@ -310,7 +310,6 @@ __device__ __forceinline__ float e8m0_f32(uint32_t c) { return __builtin_bit_cas
 // i from byte i.  Exact while the product is a normal or subnormal BF16
 // value with its bits intact: scale codes 3..246.
 __device__ __forceinline__ bf16x8 widen8_bf16(uint32_t w0, uint32_t w1, float s) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
   const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
@@ -346,15 +345,10 @@ __device__ __forceinline__ void store4(void* c, int64_t ldc, int64_t m, int64_t 
     }
   } else {
     __bf16* p = static_cast<__bf16*>(c) + m * ldc + n;
-    const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
     if (n + 3 < N && ((reinterpret_cast<uintptr_t>(p) & 7) == 0)) {
-      uint2 u;
-      u.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-      u.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-      *reinterpret_cast<uint2*>(p) = u;
+      *reinterpret_cast<uint2*>(p) = make_uint2(bf16x2_bits(v0, v1), bf16x2_bits(v2, v3));
     } else {
+      const __bf16 b0 = (__bf16)v0, b1 = (__bf16)v1, b2 = (__bf16)v2, b3 = (__bf16)v3;
       if (n < N) p[0] = b0;
       if (n + 1 < N) p[1] = b1;
       if (n + 2 < N) p[2] = b2;
@@ -1029,12 +1023,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const f32x16& v = acc[i][j];
-            uint2 u;
-            u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 1]) << 16);
-            u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 2]) |
-                  ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[4 * q + 3]) << 16);
-            *reinterpret_cast<uint2*>(smem + ml * kCStride + (j * 128 + cl) * 2) = u;
+            *reinterpret_cast<uint2*>(smem + ml * kCStride + (j * 128 + cl) * 2) =
+                make_uint2(bf16x2_bits(v[4 * q], v[4 * q + 1]), bf16x2_bits(v[4 * q + 2], v[4 * q + 3]));
           }
         }
       barrier();
@@ -1056,30 +1046,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
       // h in BF16 (the per-group quantizer's input), staged as [256 rows][128
       // columns], and the group's largest |h| as an FP32 bit pattern
       // (magnitudes order as integers; NaN above Inf above finite values).
-      uint32_t am = 0;
+      u16x2 am2 = __builtin_bit_cast(u16x2, 0u);    // largest |h| bit patterns, per half
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ml = wm * 128 + i * 32 + r32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t hbits[4];
+          float hv[4];
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const float hv = silu_f32(acc[i][0][4 * q + e4]) * acc[i][1][4 * q + e4];
-            hbits[e4] = __builtin_bit_cast(uint16_t, (__bf16)hv);
-          }
+          for (int e4 = 0; e4 < 4; ++e4) hv[e4] = silu_f32(acc[i][0][4 * q + e4]) * acc[i][1][4 * q + e4];
+          const uint2 u = make_uint2(bf16x2_bits(hv[0], hv[1]), bf16x2_bits(hv[2], hv[3]));
           const bool live = ml < rows_t && hct + hb + q * 8 + half * 4 < F;
-#pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const uint32_t m = live ? (hbits[e4] & 0x7FFFu) : 0u;
-            am = am > m ? am : m;
+          if (live) {
+            am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2, u.x & 0x7FFF7FFFu));
+            am2 = __builtin_elementwise_max(am2, __builtin_bit_cast(u16x2, u.y & 0x7FFF7FFFu));
           }
-          uint2 u;
-          u.x = hbits[0] | (hbits[1] << 16);
-          u.y = hbits[2] | (hbits[3] << 16);
           *reinterpret_cast<uint2*>(smem + ml * kCStride + (hb + q * 8 + half * 4) * 2) = u;
         }
       }
+      uint32_t am = am2.x > am2.y ? am2.x : am2.y;
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)am, sh, 64);
@@ -1202,12 +1187,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g) {
         for (int q = 0; q < 4; ++q) {
           const int ml = wm * RW + i * 32 + r32, nl = bn + j * 32 + q * 8 + half * 4;
           const f32x16& v = acc[i][j];
-          uint2 u;
-          u.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q] * mul)) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 1] * mul)) << 16);
-          u.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 2] * mul)) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[4 * q + 3] * mul)) << 16);
-          *reinterpret_cast<uint2*>(smem + ml * kCStride + nl * 2) = u;
+          *reinterpret_cast<uint2*>(smem + ml * kCStride + nl * 2) =
+              make_uint2(bf16x2_bits(v[4 * q] * mul, v[4 * q + 1] * mul),
+                         bf16x2_bits(v[4 * q + 2] * mul, v[4 * q + 3] * mul));
         }
     barrier();
     const int rsub = lane >> 5, col = lane & 31;
