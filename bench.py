@@ -184,13 +184,14 @@ def main():
     T = Timer(torch)
 
     def step_dual():
-        # forward (each tensor's row and column copies come from one pass)
-        xq, xs, xT, xTs, poff = T.run("q_dual", mxq.mx_quantize_dual, X, offs_d)
-        wq, ws, guT, guTs, _ = T.run("q_dual", mxq.mx_quantize_dual, Wgu, w_off_gu)
+        # forward (each tensor's row and column copies come from one pass; a
+        # product's activation and expert weights are quantized in one launch)
+        (xq, xs, xT, xTs, poff), (wq, ws, guT, guTs, _) = T.run(
+            "q_dual", mxq.mx_quantize_dual_batch, [(X, offs_d), (Wgu, w_off_gu)])
         gu = T.run("gmm", mxq.mx_grouped_gemm, xq, xs, wq.view(E, 2 * FFN, HIDDEN),
                    ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
-        hq, hs, hT, hTs, _ = T.run("q_dual", mxq.mx_quantize_dual, h, offs_d)
-        dq, dsc, dnT, dnTs, _ = T.run("q_dual", mxq.mx_quantize_dual, Wdn, w_off_dn)
+        (hq, hs, hT, hTs, _), (dq, dsc, dnT, dnTs, _) = T.run(
+            "q_dual", mxq.mx_quantize_dual_batch, [(h, offs_d), (Wdn, w_off_dn)])
         y = T.run("gmm", mxq.mx_grouped_gemm, hq, hs, dq.view(E, HIDDEN, FFN),
                   dsc.view(E, HIDDEN, FFN // 32), offs_d)
         # dgrad
@@ -358,7 +359,8 @@ def main():
                    "max_expert_rows": int(counts.max()), "min_expert_rows": int(counts.min()),
                    "weights_quantized_each_step": True,
                    "quantization": "separate row and column passes" if args.separate_quant
-                   else "dual-axis (one pass per tensor)",
+                   else "dual-axis (one pass per tensor; each product's activation and "
+                   "expert weights in one launch)",
                    "algorithmic_flops": flops},
         "pct_mx_fp8_peak": 100.0 * value / PEAK_MFMA_TFLOPS,
         "roofline": roof,
@@ -512,12 +514,12 @@ def exact_mode(torch, mxq, workloads, to_dev, seed, X, h, Wgu, Wdn, dY, dGU, off
     ACC = mxq.ACC_FP32
 
     def step():
-        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(X, offs_d)
-        wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(Wgu, w_off_gu)
+        (xq, xs, xT, xTs, poff), (wq, ws, guT, guTs, _) = mxq.mx_quantize_dual_batch(
+            [(X, offs_d), (Wgu, w_off_gu)])
         mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
                             ws.view(E, 2 * FFN, HIDDEN // 32), offs_d, accum=ACC)
-        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(h, offs_d)
-        dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(Wdn, w_off_dn)
+        (hq, hs, hT, hTs, _), (dq, dsc, dnT, dnTs, _) = mxq.mx_quantize_dual_batch(
+            [(h, offs_d), (Wdn, w_off_dn)])
         mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
                             offs_d, accum=ACC)
         gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(dY, offs_d)
@@ -692,8 +694,8 @@ def fused_producer(torch, mxq, X, Wgu, Wdn, dY, dGU, offs_d, w_off_gu, w_off_dn,
 
     def full_step():
         # the step's own quantization of X and W_gu, then the rest
-        xq_s[:] = mxq.mx_quantize_dual(X, offs_d)[:4]
-        q = mxq.mx_quantize_dual(Wgu, w_off_gu)
+        xo, q = mxq.mx_quantize_dual_batch([(X, offs_d), (Wgu, w_off_gu)])
+        xq_s[:] = xo[:4]
         wgu_s[:] = [q[0].view(E, 2 * FFN, HIDDEN), q[1].view(E, 2 * FFN, HIDDEN // 32)]
         wqT_s[:] = [q[2], q[3]]
         step()
@@ -841,20 +843,34 @@ def full_block_step(torch, mxq, workloads, seed):
         return qw, mxq.mx_quantize_dual(Wgu, w_off_gu), mxq.mx_quantize_dual(Wdn, w_off_dn)
 
     def step(wts=None):
-        qw, qgu, qdn = wts if wts is not None else quant_weights()
-        for d, (wq, ws, wT, wTs, _) in zip(dense, qw):
+        # in the step, each product's input and weight are quantized in one launch
+        qw, qgu, qdn = wts if wts is not None else (None, None, None)
+        for i, d in enumerate(dense):
             fout = d["fout"]
-            xq, xs, xT, xTs, _ = mxq.mx_quantize_dual(d["X"], one)
+            if qw is None:
+                (xq, xs, xT, xTs, _), (wq, ws, wT, wTs, _) = mxq.mx_quantize_dual_batch(
+                    [(d["X"], one), (d["W"], d["woff"])])
+            else:
+                wq, ws, wT, wTs, _ = qw[i]
+                xq, xs, xT, xTs, _ = mxq.mx_quantize_dual(d["X"], one)
             gq, gs, gT, gTs, _ = mxq.mx_quantize_dual(d["dY"], one)
             mxq.mx_gemm(xq, xs, wq, ws)                                    # Y = X Wᵀ
             mxq.mx_gemm(gq, gs, wT[:, :fout], wTs[:, :fout // 32])         # dX = dY W
             mxq.mx_gemm(gT[:, :T], gTs[:, :T // 32], xT[:, :T], xTs[:, :T // 32])  # dW
-        wq, ws, guT, guTs, _ = qgu
-        dq, dsc, dnT, dnTs, _ = qdn
-        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(rX, offs_d)
+        if qgu is None:
+            (xq, xs, xT, xTs, poff), (wq, ws, guT, guTs, _) = mxq.mx_quantize_dual_batch(
+                [(rX, offs_d), (Wgu, w_off_gu)])
+        else:
+            wq, ws, guT, guTs, _ = qgu
+            xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(rX, offs_d)
         mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * FFN, HIDDEN),
                             ws.view(E, 2 * FFN, HIDDEN // 32), offs_d)
-        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(rh, offs_d)
+        if qdn is None:
+            (hq, hs, hT, hTs, _), (dq, dsc, dnT, dnTs, _) = mxq.mx_quantize_dual_batch(
+                [(rh, offs_d), (Wdn, w_off_dn)])
+        else:
+            dq, dsc, dnT, dnTs, _ = qdn
+            hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(rh, offs_d)
         mxq.mx_grouped_gemm(hq, hs, dq.view(E, HIDDEN, FFN), dsc.view(E, HIDDEN, FFN // 32),
                             offs_d)
         gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(rdY, offs_d)

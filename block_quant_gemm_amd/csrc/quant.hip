@@ -200,14 +200,16 @@ constexpr int kRowStageW = kRowStage * kColTileK + 16;  // LDS row stride (bytes
 // PG (per-group current scaling, transposed copy): no block scales; every
 // 32-row block takes its group's FP32 scale (gscale, with gmax the group's
 // |x| maximum pattern) and encodes as the per-tensor pass does.
-template <bool ROW, bool PG = false>
-__global__ __launch_bounds__(256) void k_mx_colwise(
+// bid / nblk: this workgroup's index among its matrix's nblk workgroups.
+template <bool ROW, bool PG>
+__device__ __forceinline__ void colwise_body(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
     const int64_t* __restrict__ offsets, int32_t E,
     uint8_t* __restrict__ qT, int64_t ldqT, int64_t M_cap,
     uint8_t* __restrict__ scT, int64_t ldsT, int64_t* __restrict__ offsets_padded,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ sc, int64_t lds,
-    const uint32_t* __restrict__ gmax = nullptr, const float* __restrict__ gscale = nullptr) {
+    const uint32_t* __restrict__ gmax, const float* __restrict__ gscale, uint32_t bid,
+    uint32_t nblk) {
   __shared__ uint32_t tile[kColTileM * kColLdsW];
   __shared__ __attribute__((aligned(16))) uint8_t outq[kColTileK * kColOutW];
   __shared__ __attribute__((aligned(16))) uint8_t outs[kColTileK * 4];
@@ -228,14 +230,14 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
   const uint32_t nky = (uint32_t)((K + kColTileK * kColPasses - 1) / (kColTileK * kColPasses));
   uint32_t bx, by;
   if (ROW) {
-    const uint32_t ngx = gridDim.x / nky, G = kColDualGroup;
-    const uint32_t per = G * nky, grp = blockIdx.x / per, in = blockIdx.x % per;
+    const uint32_t ngx = nblk / nky, G = kColDualGroup;
+    const uint32_t per = G * nky, grp = bid / per, in = bid % per;
     const uint32_t gw = ngx - grp * G < G ? ngx - grp * G : G;
     bx = grp * G + in % gw;
     by = in / gw;
   } else {
-    bx = blockIdx.x / nky;
-    by = blockIdx.x % nky;
+    bx = bid / nky;
+    by = bid % nky;
   }
   const int64_t p0 = (int64_t)bx * kColTileM;             // first padded column
   const int64_t kw0 = (int64_t)by * kColTileK * kColPasses;  // first input column
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
     }
   }
   __syncthreads();
-  if (offsets_padded && blockIdx.x == 0)
+  if (offsets_padded && bid == 0)
     for (int g = tid; g <= G; g += blockDim.x) offsets_padded[g] = s_poff[g];
   if (tid < 4) {
     // Source rows of 32-block tid of this tile: find g with
@@ -483,6 +485,46 @@ __global__ __launch_bounds__(256) void k_mx_colwise(
       nxt[u] = nx2[u];
     }
   }
+}
+
+// Up to kColBatch matrices in one launch (each with its own groups and
+// outputs): item i owns workgroups [first, first + nblk) of the grid.
+constexpr int kColBatch = MXQ_DUAL_BATCH_MAX;
+struct ColItem {
+  const uint16_t* x;
+  int64_t M, K, ldx;
+  const int64_t* offsets;
+  uint8_t* qT;
+  int64_t ldqT, M_cap;
+  uint8_t* scT;
+  int64_t ldsT;
+  int64_t* offsets_padded;
+  uint8_t* q;
+  int64_t ldq;
+  uint8_t* sc;
+  int64_t lds;
+  const uint32_t* gmax;
+  const float* gscale;
+  int32_t E;
+  uint32_t first, nblk;
+};
+struct ColBatch {
+  ColItem it[kColBatch];
+  uint32_t n;
+};
+
+template <bool ROW, bool PG = false>
+__global__ __launch_bounds__(256) void k_mx_colwise(ColBatch b) {
+  // the item of this workgroup (items in order of first)
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kColBatch; ++k)
+    if ((uint32_t)k < b.n && blockIdx.x >= b.it[k].first) i = k;
+  const ColItem t = i == 0 ? b.it[0] : i == 1 ? b.it[1] : i == 2 ? b.it[2] : b.it[3];
+  static_assert(kColBatch == 4, "item selection above");
+  colwise_body<ROW, PG>(t.x, t.M, t.K, t.ldx, t.offsets, t.E, t.qT, t.ldqT, t.M_cap, t.scT, t.ldsT,
+                        t.offsets_padded, t.q, t.ldq, t.sc, t.lds, t.gmax, t.gscale,
+                        blockIdx.x - t.first, t.nblk);
 }
 
 // ---------------------------------------------------------------------------
@@ -912,6 +954,36 @@ static int64_t padded_capacity(int64_t M, int32_t E) {
   return E > 0 ? sat_add(M, 31LL * E) : sat_add(M, 31) / 32 * 32;
 }
 
+// Workgroups of one column-tile item: M_cap in 128-column tiles times K in
+// chunks of kColPasses passes.
+static int col_blocks(int64_t M_cap, int64_t K, uint32_t* nblk) {
+  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
+  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
+  const int64_t n = sat_mul(gx, gy);
+  if (n > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+  *nblk = (uint32_t)n;
+  return MXQ_OK;
+}
+
+template <bool ROW, bool PG>
+static int launch_colwise(ColBatch& b, hipStream_t stream) {
+  // pack the non-empty items, each owning a contiguous run of workgroups
+  uint32_t n = 0;
+  int64_t first = 0;
+  for (uint32_t i = 0; i < b.n; ++i) {
+    if (b.it[i].nblk == 0) continue;
+    b.it[n] = b.it[i];
+    b.it[n].first = (uint32_t)first;
+    first += b.it[i].nblk;
+    if (first > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
+    ++n;
+  }
+  if (n == 0) return MXQ_OK;
+  b.n = n;
+  hipLaunchKernelGGL((k_mx_colwise<ROW, PG>), dim3((uint32_t)first), dim3(256), 0, stream, b);
+  return launch_status();
+}
+
 extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    const int64_t* offsets, int32_t E, uint8_t* qT, int64_t ldqT,
                                    int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
@@ -925,20 +997,23 @@ extern "C" int mx_quantize_colwise(const uint16_t* x, int64_t M, int64_t K, int6
     return MXQ_ERR_SHAPE;
   if (ldqT % 16 != 0 || ldx % 8 != 0 || !aligned(qT, 16) || (x && !aligned(x, 16)))
     return MXQ_ERR_ALIGN;
-  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
-  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
-  dim3 grid((uint32_t)(gx * gy));
-  hipLaunchKernelGGL(k_mx_colwise<false>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
-                     qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, nullptr, 0, nullptr, 0);
-  return launch_status();
+  ColBatch b{};
+  ColItem& t = b.it[0];
+  if (col_blocks(M_cap, K, &t.nblk) != MXQ_OK) return MXQ_ERR_SHAPE;
+  t.x = x; t.M = M; t.K = K; t.ldx = ldx; t.offsets = offsets; t.E = E;
+  t.qT = qT; t.ldqT = ldqT; t.M_cap = M_cap; t.scT = scaleT; t.ldsT = ldsT;
+  t.offsets_padded = offsets_padded;
+  b.n = 1;
+  return launch_colwise<false, false>(b, stream);
 }
 
-extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                const int64_t* offsets, int32_t E, uint8_t* q, int64_t ldq,
-                                uint8_t* scale, int64_t lds, uint8_t* qT, int64_t ldqT,
-                                int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
-                                int64_t* offsets_padded, hipStream_t stream) {
+// Checks one dual-axis item and fills it (nblk == 0 for an item that writes
+// nothing).
+static int dual_item(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     const int64_t* offsets, int32_t E, uint8_t* q, int64_t ldq, uint8_t* scale,
+                     int64_t lds, uint8_t* qT, int64_t ldqT, int64_t M_cap, uint8_t* scaleT,
+                     int64_t ldsT, int64_t* offsets_padded, ColItem* t) {
+  *t = ColItem{};
   if (M < 0 || K < 0 || M_cap < 0) return MXQ_ERR_SHAPE;
   if (offsets && (E < 1 || E > kColMaxGroupsLds)) return MXQ_ERR_SHAPE;
   // every row must land in the column copy: the row copy is written from the
@@ -952,13 +1027,42 @@ extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t
   if (ldqT % 16 != 0 || ldx % 8 != 0 || ldq % 16 != 0 || !aligned(qT, 16) ||
       (x && !aligned(x, 16)) || (q && !aligned(q, 16)))
     return MXQ_ERR_ALIGN;
-  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
-  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
-  dim3 grid((uint32_t)(gx * gy));
-  hipLaunchKernelGGL(k_mx_colwise<true>, grid, dim3(256), 0, stream, x, M, K, ldx, offsets, E,
-                     qT, ldqT, M_cap, scaleT, ldsT, offsets_padded, q, ldq, scale, lds);
-  return launch_status();
+  uint32_t nblk = 0;
+  if (col_blocks(M_cap, K, &nblk) != MXQ_OK) return MXQ_ERR_SHAPE;
+  t->x = x; t->M = M; t->K = K; t->ldx = ldx; t->offsets = offsets; t->E = E;
+  t->qT = qT; t->ldqT = ldqT; t->M_cap = M_cap; t->scT = scaleT; t->ldsT = ldsT;
+  t->offsets_padded = offsets_padded;
+  t->q = q; t->ldq = ldq; t->sc = scale; t->lds = lds;
+  t->nblk = nblk;
+  return MXQ_OK;
+}
+
+extern "C" int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const int64_t* offsets, int32_t E, uint8_t* q, int64_t ldq,
+                                uint8_t* scale, int64_t lds, uint8_t* qT, int64_t ldqT,
+                                int64_t M_cap, uint8_t* scaleT, int64_t ldsT,
+                                int64_t* offsets_padded, hipStream_t stream) {
+  ColBatch b{};
+  const int st = dual_item(x, M, K, ldx, offsets, E, q, ldq, scale, lds, qT, ldqT, M_cap, scaleT,
+                           ldsT, offsets_padded, &b.it[0]);
+  if (st != MXQ_OK) return st;
+  b.n = 1;
+  return launch_colwise<true, false>(b, stream);
+}
+
+extern "C" int mx_quantize_dual_batch(const mxq_dual_item* items, int32_t n,
+                                      hipStream_t stream) {
+  if (n < 1 || n > kColBatch) return MXQ_ERR_SHAPE;
+  if (!items) return MXQ_ERR_NULL;
+  ColBatch b{};
+  for (int32_t i = 0; i < n; ++i) {
+    const mxq_dual_item& d = items[i];
+    const int st = dual_item(d.x, d.M, d.K, d.ldx, d.offsets, d.E, d.q, d.ldq, d.scale, d.lds,
+                             d.qT, d.ldqT, d.M_cap, d.scaleT, d.ldsT, d.offsets_padded, &b.it[i]);
+    if (st != MXQ_OK) return st;
+  }
+  b.n = (uint32_t)n;
+  return launch_colwise<true, false>(b, stream);
 }
 
 extern "C" size_t mxq_workspace_size(int op, int64_t n, int64_t a1, int64_t, int64_t) {
@@ -1127,13 +1231,14 @@ static int quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K, i
                                                              : waves / 4);
   int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
-  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
-  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
-  hipLaunchKernelGGL((k_mx_colwise<false, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
-                     x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded,
-                     nullptr, 0, nullptr, 0, gmax, scales);
-  return launch_status();
+  ColBatch b{};
+  ColItem& t = b.it[0];
+  if (col_blocks(M_cap, K, &t.nblk) != MXQ_OK) return MXQ_ERR_SHAPE;
+  t.x = x; t.M = M; t.K = K; t.ldx = ldx; t.offsets = offsets; t.E = E;
+  t.qT = qT; t.ldqT = ldqT; t.M_cap = M_cap; t.offsets_padded = offsets_padded;
+  t.gmax = gmax; t.gscale = scales;
+  b.n = 1;
+  return launch_colwise<false, true>(b, stream);
 }
 
 extern "C" int fp8_quantize_per_group_colwise(const uint16_t* x, int64_t M, int64_t K,
@@ -1187,13 +1292,14 @@ extern "C" int fp8_quantize_per_group_dual(const uint16_t* x, int64_t M, int64_t
                                                              : waves / 4);
   int st = pg_scales(x, M, K, ldx, offsets, E, amax, rowmax, gmax, scales, blocks, stream);
   if (st != MXQ_OK || K == 0 || M_cap == 0) return st;
-  const int64_t gx = sat_add(M_cap, kColTileM - 1) / kColTileM;
-  const int64_t gy = sat_add(K, kColTileK * kColPasses - 1) / (kColTileK * kColPasses);
-  if (sat_mul(gx, gy) > 0x7FFFFFFFLL) return MXQ_ERR_SHAPE;
-  hipLaunchKernelGGL((k_mx_colwise<true, true>), dim3((uint32_t)(gx * gy)), dim3(256), 0, stream,
-                     x, M, K, ldx, offsets, E, qT, ldqT, M_cap, nullptr, 0, offsets_padded, q, ldq,
-                     nullptr, 0, gmax, scales);
-  return launch_status();
+  ColBatch b{};
+  ColItem& t = b.it[0];
+  if (col_blocks(M_cap, K, &t.nblk) != MXQ_OK) return MXQ_ERR_SHAPE;
+  t.x = x; t.M = M; t.K = K; t.ldx = ldx; t.offsets = offsets; t.E = E;
+  t.qT = qT; t.ldqT = ldqT; t.M_cap = M_cap; t.offsets_padded = offsets_padded;
+  t.q = q; t.ldq = ldq; t.gmax = gmax; t.gscale = scales;
+  b.n = 1;
+  return launch_colwise<true, true>(b, stream);
 }
 
 extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, float* scale,

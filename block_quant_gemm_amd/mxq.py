@@ -21,6 +21,7 @@ WS_PER_TENSOR, WS_PER_GROUP = 0, 1
 
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
 ROWWISE_BATCH_MAX = 4
+DUAL_BATCH_MAX = 4
 
 
 class RowwiseItem(ctypes.Structure):
@@ -29,11 +30,20 @@ class RowwiseItem(ctypes.Structure):
                 ("scale", _p), ("lds", _i64)]
 
 
+class DualItem(ctypes.Structure):
+    """mxq_dual_item of mxq.h."""
+    _fields_ = [("x", _p), ("M", _i64), ("K", _i64), ("ldx", _i64), ("offsets", _p),
+                ("E", _i32), ("q", _p), ("ldq", _i64), ("scale", _p), ("lds", _i64),
+                ("qT", _p), ("ldqT", _i64), ("M_cap", _i64), ("scaleT", _p), ("ldsT", _i64),
+                ("offsets_padded", _p)]
+
+
 _SIGS = {
     "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mxq_version": (ctypes.c_int, []),
     "mx_quantize_rowwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "mx_quantize_rowwise_batch": (ctypes.c_int, [ctypes.POINTER(RowwiseItem), _i32, _p]),
+    "mx_quantize_dual_batch": (ctypes.c_int, [ctypes.POINTER(DualItem), _i32, _p]),
     "mx_quantize_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _i64,
                                            _p, _i64, _p, _p]),
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _i64,
@@ -214,6 +224,17 @@ def mx_quantize_dual(x, offsets=None, M_cap=None, q=None, scale=None, qT=None, s
     Returns (codes [M, K], scales [M, K/32], codesT [K, M_cap],
     scalesT [K, M_cap/32], offsets_padded or None), each equal to what
     mx_quantize_rowwise / mx_quantize_colwise return."""
+    x, E, M_cap, q, scale, qT, scaleT, offsets_padded = _dual_outputs(
+        x, offsets, M_cap, q, scale, qT, scaleT, offsets_padded)
+    M, K = x.shape
+    _check(load().mx_quantize_dual(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q),
+                                   q.stride(0), _ptr(scale), scale.stride(0), _ptr(qT),
+                                   qT.stride(0), M_cap, _ptr(scaleT), scaleT.stride(0),
+                                   _ptr(offsets_padded), _stream()))
+    return q, scale, qT, scaleT, offsets_padded
+
+
+def _dual_outputs(x, offsets, M_cap, q, scale, qT, scaleT, offsets_padded):
     x = _bf16_bits(x)
     M, K = x.shape
     E = 0 if offsets is None else offsets.numel() - 1
@@ -229,11 +250,26 @@ def mx_quantize_dual(x, offsets=None, M_cap=None, q=None, scale=None, qT=None, s
         scaleT = _scale_buffer(K, M_cap // 32, x.device)
     if offsets is not None and offsets_padded is None:
         offsets_padded = torch.empty(E + 1, dtype=torch.int64, device=x.device)
-    _check(load().mx_quantize_dual(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q),
-                                   q.stride(0), _ptr(scale), scale.stride(0), _ptr(qT),
-                                   qT.stride(0), M_cap, _ptr(scaleT), scaleT.stride(0),
-                                   _ptr(offsets_padded), _stream()))
-    return q, scale, qT, scaleT, offsets_padded
+    return x, E, M_cap, q, scale, qT, scaleT, offsets_padded
+
+
+def mx_quantize_dual_batch(items):
+    """Dual-axis MX quantization of several BF16 matrices in one launch (e.g.
+    an expert product's activation and its stacked weights).  items: a list of
+    (x, offsets) pairs, offsets None for one group.  Returns one
+    (codes, scales, codesT, scalesT, offsets_padded) tuple per item, as
+    mx_quantize_dual would."""
+    outs, arr = [], (DualItem * len(items))()
+    for i, (x, offsets) in enumerate(items):
+        x, E, M_cap, q, scale, qT, scaleT, poff = _dual_outputs(
+            x, offsets, None, None, None, None, None, None)
+        M, K = x.shape
+        arr[i] = DualItem(_ptr(x), M, K, x.stride(0), _ptr(offsets), E, _ptr(q), q.stride(0),
+                          _ptr(scale), scale.stride(0), _ptr(qT), qT.stride(0), M_cap,
+                          _ptr(scaleT), scaleT.stride(0), _ptr(poff))
+        outs.append((x, q, scale, qT, scaleT, poff))
+    _check(load().mx_quantize_dual_batch(arr, len(items), _stream()))
+    return [o[1:] for o in outs]
 
 
 def workspace_size(op, n, a1=0, a2=0, a3=0):

@@ -164,6 +164,36 @@ MXQ_API int mx_quantize_dual(const uint16_t* x, int64_t M, int64_t K, int64_t ld
                      int64_t* offsets_padded, hipStream_t stream);
 
 /*
+ * Several dual-axis MX quantizations in one launch, each with its own groups,
+ * e.g. a product's activation and its expert weights, whose forward product
+ * reads both row copies and whose backward products read the column copies
+ * ([HP329] §8 direction table; §8.1 activations and weights each keep both
+ * copies).  Each item receives exactly the outputs mx_quantize_dual gives it,
+ * under the same requirements; an item with K == 0 or M_cap == 0 is skipped.
+ *   items : host array of n items, read during the call only.
+ *   n     : 1 .. MXQ_DUAL_BATCH_MAX (else MXQ_ERR_SHAPE).
+ * The first item that fails a check decides the returned status and nothing
+ * is launched.  Items must not write overlapping memory.
+ */
+#define MXQ_DUAL_BATCH_MAX 4
+typedef struct mxq_dual_item {
+  const uint16_t* x;         /* device, BF16 [M, K], row stride ldx elements */
+  int64_t M, K, ldx;
+  const int64_t* offsets;    /* device int64 [E+1] or NULL, as for mx_quantize_colwise */
+  int32_t E;
+  uint8_t* q;                /* row copy: E4M3 [M, K], row stride ldq bytes */
+  int64_t ldq;
+  uint8_t* scale;            /* row copy: E8M0 [M, K/32], row stride lds bytes */
+  int64_t lds;
+  uint8_t* qT;               /* column copy: E4M3 [K, ldqT], M_cap columns written */
+  int64_t ldqT, M_cap;
+  uint8_t* scaleT;           /* column copy: E8M0 [K, ldsT] */
+  int64_t ldsT;
+  int64_t* offsets_padded;   /* device int64 [E+1] receiving poff, or NULL */
+} mxq_dual_item;
+MXQ_API int mx_quantize_dual_batch(const mxq_dual_item* items, int32_t n, hipStream_t stream);
+
+/*
  * Per-tensor current-scaling FP8 E4M3 ([HP329] §3.2 current scaling: FP32
  * scale s = amax / 448 when amax is finite and non-zero, else s = 1;
  * [FPBLOG] §七.2 first pass finds amax, second pass quantizes).

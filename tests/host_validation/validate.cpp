@@ -93,6 +93,38 @@ int main() {
          MXQ_ERR_SHAPE);
   EXPECT(mx_quantize_dual(X, 64, 32, 32, O, 0, P, 32, P, 16, P, 192, 192, P, 16, O, nullptr),
          MXQ_ERR_SHAPE);
+  // ---- dual-axis, several matrices in one launch ----
+  {
+    const mxq_dual_item good{X, 64, 32, 32, O, 4, P, 32, P, 16, P, 192, 192, P, 16, O};
+    const mxq_dual_item small_cap{X, 64, 32, 32, O, 4, P, 32, P, 16, P, 160, 160, P, 16, O};
+    const mxq_dual_item no_groups{X, 64, 32, 32, O, 0, P, 32, P, 16, P, 192, 192, P, 16, O};
+    const mxq_dual_item odd{X + 1, 64, 32, 32, O, 4, P, 32, P, 16, P, 192, 192, P, 16, O};
+    const mxq_dual_item null_qt{X, 64, 32, 32, O, 4, P, 32, P, 16, nullptr, 192, 192, P, 16, O};
+    const mxq_dual_item empty{nullptr, 0, 0, 0, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0,
+                              0, nullptr, 0, nullptr};
+    // 2^38 output columns of one K chunk: 2^31 column tiles
+    const mxq_dual_item huge{nullptr, 0, 256, 256, nullptr, 0, nullptr, 256, nullptr, 8, P,
+                             INT64_C(1) << 38, INT64_C(1) << 38, P, INT64_C(1) << 33, nullptr};
+    // 2^30 workgroups each, so two pass 2^31 together
+    const mxq_dual_item half{nullptr, 0, 256, 256, nullptr, 0, nullptr, 256, nullptr, 8, P,
+                             INT64_C(1) << 37, INT64_C(1) << 37, P, INT64_C(1) << 32, nullptr};
+    const mxq_dual_item five[5] = {good, good, good, good, good};
+    EXPECT(mx_quantize_dual_batch(five, 0, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(five, 5, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(nullptr, 1, nullptr), MXQ_ERR_NULL);
+    const mxq_dual_item a[2] = {good, small_cap}, b2[2] = {odd, good}, c[2] = {empty, empty};
+    const mxq_dual_item d[2] = {good, huge}, e[2] = {half, half}, f[3] = {empty, half, good};
+    const mxq_dual_item g2[2] = {good, no_groups}, h2[2] = {null_qt, good};
+    EXPECT(mx_quantize_dual_batch(a, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(b2, 2, nullptr), MXQ_ERR_ALIGN);
+    EXPECT(mx_quantize_dual_batch(c, 2, nullptr), MXQ_OK);      // nothing to launch
+    EXPECT(mx_quantize_dual_batch(d, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(e, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(g2, 2, nullptr), MXQ_ERR_SHAPE);
+    EXPECT(mx_quantize_dual_batch(h2, 2, nullptr), MXQ_ERR_NULL);
+    EXPECT(mx_quantize_dual_batch(f, 3, nullptr), HIP);
+    EXPECT(mx_quantize_dual_batch(five, 4, nullptr), HIP);
+  }
   // ---- per-tensor and per-group ----
   EXPECT(fp8_quantize_per_tensor(X, -5, P, Fp, P, 4096, nullptr), MXQ_ERR_SHAPE);
   EXPECT(fp8_quantize_per_tensor(X, 100, P, Fp, P, 4, nullptr), MXQ_ERR_WORKSPACE);

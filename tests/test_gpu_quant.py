@@ -289,6 +289,53 @@ def test_dual_matches_single_axis_calls_full_size():
     assert np.array_equal(host(qT[ci])[:, :Mp], cc) and np.array_equal(host(sT[ci])[:, :Mp // 32], cs)
 
 
+def test_dual_batch_equals_single_calls():
+    """One launch for several matrices with their own groups: an activation
+    with empty and one-row experts, a weight stack with offsets e*N (N/32 odd,
+    so each expert's column scales start mid-word), one group of all rows, an
+    empty grouped item (only the column copy's zero padding) and K = 1408
+    (a half-full last K chunk): every output of each item is bit-equal to its
+    own mx_quantize_dual call, and the oracle checks the row and grouped column
+    copies of every item."""
+    say("dual batch: 300-row activation in 7 groups, 3x96-row weight stack, "
+        "200x1408 one group, empty grouped; then 2 items")
+    counts = np.array([40, 0, 1, 32, 0, 226, 1], np.int64)
+    offs = workloads.offsets_from_counts(counts)
+    a = workloads.bf16_normal((300, 224), 1.0, seed=21, name="db_a", outlier_frac=0.01,
+                              outlier_scale=100.0)
+    w = workloads.bf16_normal((3 * 96, 224), 0.02, seed=22, name="db_w")
+    w_offs = np.arange(4, dtype=np.int64) * 96
+    h = workloads.bf16_normal((200, 1408), 1.0, seed=23, name="db_h")
+    e_offs = np.zeros(3, np.int64)
+    items = [(to_dev_bf16(a), to_dev(offs)), (to_dev_bf16(w), to_dev(w_offs)),
+             (to_dev_bf16(h), None),
+             (torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), to_dev(e_offs))]
+    outs = mxq.mx_quantize_dual_batch(items)
+    outs += mxq.mx_quantize_dual_batch(items[1:3])
+    hosts = [(a, offs), (w, w_offs), (h, None), (None, e_offs), (w, w_offs), (h, None)]
+    for i, ((x, o), (xh, oh), out) in enumerate(zip(items + items[1:3], hosts, outs)):
+        single = mxq.mx_quantize_dual(x, o)
+        for j, (u, v) in enumerate(zip(out, single)):
+            if u is None:
+                assert v is None
+            else:
+                assert torch.equal(u, v), f"item {i} output {j} differs from its own call"
+        q, sc, qT, sT, poff = out
+        if xh is None:
+            assert np.array_equal(host(poff), oh)
+            assert int(host(qT).max(initial=0)) == 0 and int(host(sT).max(initial=0)) == 0
+            continue
+        rc, rs = mx.mx_quantize_rowwise(xh)
+        assert np.array_equal(host(q), rc) and np.array_equal(host(sc), rs), f"item {i} row copy"
+        go = oh if oh is not None else np.array([0, xh.shape[0]], np.int64)
+        cc, cs, rpoff = mx.mx_quantize_grouped_colwise(xh, go)
+        Mp = int(rpoff[-1])
+        assert np.array_equal(host(qT)[:, :Mp], cc) and np.array_equal(host(sT)[:, :Mp // 32], cs), \
+            f"item {i} column copy"
+        if oh is not None:
+            assert np.array_equal(host(poff), rpoff)
+
+
 # ---------------------------------------------------------------------------
 # per-tensor
 # ---------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 and its host-side argument checks reject bad calls without touching a GPU.
 CPU only (no kernel is launched)."""
 
+import ctypes
 import os
 import re
 
@@ -110,6 +111,30 @@ def test_rowwise_batch_validation_errors(host_only_lib):
     empty = It(None, 0, 32, 32, None, 32, None, 1)
     assert call(empty, empty) == 0                                  # nothing to launch
     assert mxq.ROWWISE_BATCH_MAX == 4
+
+
+def test_dual_batch_validation_errors(host_only_lib):
+    lib = host_only_lib
+    P = 4096
+    It = mxq.DualItem
+
+    def call(*items, n=None):
+        arr = (It * len(items))(*items)
+        return lib.mx_quantize_dual_batch(arr, len(items) if n is None else n, None)
+
+    # DualItem(x, M, K, ldx, offsets, E, q, ldq, scale, lds, qT, ldqT, M_cap, scaleT, ldsT, poff)
+    good = It(P, 64, 32, 32, P, 4, P, 32, P, 16, P, 192, 192, P, 16, P)
+    assert call(good, n=0) == 2                                     # n out of range
+    assert call(*[good] * 5) == 2                                   # past the batch maximum
+    assert lib.mx_quantize_dual_batch(None, 1, None) == 1           # NULL items
+    assert call(good, It(P, 64, 32, 32, P, 4, P, 32, P, 16, P, 160, 160, P, 16, P)) == 2  # M_cap
+    assert call(It(P, 64, 40, 40, P, 4, P, 48, P, 16, P, 192, 192, P, 16, P), good) == 2  # K % 32
+    assert call(good, It(P, 64, 32, 32, P, 4, P, 32, P, 16, None, 192, 192, P, 16, P)) == 1
+    assert call(good, It(P + 2, 64, 32, 32, P, 4, P, 32, P, 16, P, 192, 192, P, 16, P)) == 3
+    empty = It(None, 0, 0, 0, None, 0, None, 0, None, 0, None, 0, 0, None, 0, None)
+    assert call(empty, empty) == 0                                  # nothing to launch
+    assert mxq.DUAL_BATCH_MAX == 4
+    assert ctypes.sizeof(It) == 128                                 # mxq_dual_item's layout
 
 
 def test_per_group_validation_errors(host_only_lib):
