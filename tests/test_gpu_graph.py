@@ -32,13 +32,21 @@ def _inputs():
                 w_off_dn=torch.arange(E + 1, dtype=torch.int64, device="cuda") * H)
 
 
-def _mx_step(d):
+def _mx_step(d, batched=False):
     o = d["offs"]
-    xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(d["X"], o)
-    wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(d["Wgu"], d["w_off_gu"])
+    if batched:     # each forward product's activation and weights in one launch
+        (xq, xs, xT, xTs, poff), (wq, ws, guT, guTs, _) = mxq.mx_quantize_dual_batch(
+            [(d["X"], o), (d["Wgu"], d["w_off_gu"])])
+    else:
+        xq, xs, xT, xTs, poff = mxq.mx_quantize_dual(d["X"], o)
+        wq, ws, guT, guTs, _ = mxq.mx_quantize_dual(d["Wgu"], d["w_off_gu"])
     gu = mxq.mx_grouped_gemm(xq, xs, wq.view(E, 2 * F, H), ws.view(E, 2 * F, H // 32), o)
-    hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(d["h"], o)
-    dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(d["Wdn"], d["w_off_dn"])
+    if batched:
+        (hq, hs, hT, hTs, _), (dq, dsc, dnT, dnTs, _) = mxq.mx_quantize_dual_batch(
+            [(d["h"], o), (d["Wdn"], d["w_off_dn"])])
+    else:
+        hq, hs, hT, hTs, _ = mxq.mx_quantize_dual(d["h"], o)
+        dq, dsc, dnT, dnTs, _ = mxq.mx_quantize_dual(d["Wdn"], d["w_off_dn"])
     y = mxq.mx_grouped_gemm(hq, hs, dq.view(E, H, F), dsc.view(E, H, F // 32), o)
     gq, gs, dyT, dyTs, _ = mxq.mx_quantize_dual(d["dY"], o)
     bq, bs = mxq.expert_view(dnT, dnTs, E, H)
@@ -49,6 +57,10 @@ def _mx_step(d):
     dwdn = mxq.mx_grouped_gemm_wgrad(dyT, dyTs, hT, hTs, poff)
     dwgu = mxq.mx_grouped_gemm_wgrad(duT, duTs, xT, xTs, poff)
     return [gu, y, dh, dx, dwdn, dwgu, xq, xT[:, :d["Mp"]]]
+
+
+def _mx_step_batched(d):
+    return _mx_step(d, batched=True)
 
 
 def _fused_and_per_group(d):
@@ -73,7 +85,7 @@ def _bits(ts):
             for t in ts]
 
 
-@pytest.mark.parametrize("step", [_mx_step, _fused_and_per_group])
+@pytest.mark.parametrize("step", [_mx_step, _mx_step_batched, _fused_and_per_group])
 def test_step_graph_replays_equal_eager(step):
     say(f"graph capture of {step.__name__}")
     d = _inputs()
