@@ -38,6 +38,27 @@ def pt_quantize(x_bf16_bits):
     return e4m3_encode(q.astype(np.float64)), np.float32(s)
 
 
+def pt_scale_of_amax(amax):
+    """The scale rule applied to an amax that is given rather than found by a
+    pass over the tensor ([FPBLOG] §七.2: the producing matmul can supply the
+    amax): fp32(amax) / fp32(448) when amax is finite and > 0, else 1.0."""
+    a = np.float32(amax)
+    if not np.isfinite(a) or a <= 0:
+        return np.float32(1.0)
+    return a / np.float32(E4M3_MAX)
+
+
+def pt_quantize_given_amax(x_bf16_bits, amax):
+    """pt_quantize with the scale taken from a given amax.  Returns (codes
+    uint8 of x's shape, scale np.float32)."""
+    bits = np.asarray(x_bf16_bits, dtype=np.uint16)
+    s = pt_scale_of_amax(amax)
+    x32 = bf16_bits_to_f64(bits).astype(np.float32)      # exact
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = x32 / np.float32(s)                          # IEEE FP32, RNE
+    return e4m3_encode(q.astype(np.float64)), np.float32(s)
+
+
 def pt_dequantize(codes, scale):
     """Exact float64 values q * scale."""
     return e4m3_decode(codes) * np.float64(np.float32(scale))

@@ -66,6 +66,41 @@ def test_nonfinite_inputs():
     assert codes.tolist() == [0x38, 0x7F, 0xFE, 0x7E, 0xC0, 0xFF]
 
 
+def test_given_amax_scale_rule():
+    """The rule of §3.2 applied to a given amax: amax / 448 in FP32 when
+    valid, 1.0 for zero, negative, NaN and infinite values."""
+    assert per_tensor.pt_scale_of_amax(896.0) == np.float32(2.0)
+    assert per_tensor.pt_scale_of_amax(1.0) == np.float32(np.float32(1.0) / np.float32(448.0))
+    for bad in (0.0, -0.0, -5.0, np.nan, np.inf, -np.inf):
+        assert per_tensor.pt_scale_of_amax(bad) == np.float32(1.0)
+
+
+def test_given_amax_equals_two_pass_at_true_amax():
+    """With the tensor's own max |x| (found here by numpy) the given-amax
+    quantization is the two-pass one, special values included."""
+    x = workloads.bf16_normal((4096,), 1.0, seed=12, name="pta", outlier_frac=0.01,
+                              outlier_scale=30.0)
+    v = codec.bf16_bits_to_f64(x)
+    c0, s0 = per_tensor.pt_quantize(x)
+    c1, s1 = per_tensor.pt_quantize_given_amax(x, np.abs(v).max())
+    assert s0 == s1 and np.array_equal(c0, c1)
+    y = np.array([0x3F80, 0x7FC0, 0xFF80, 0x7F80, 0xC000, 0xFFC0], np.uint16)
+    c2, s2 = per_tensor.pt_quantize_given_amax(y, np.nan)
+    assert s2 == 1.0 and c2.tolist() == [0x38, 0x7F, 0xFE, 0x7E, 0xC0, 0xFF]
+
+
+def test_given_amax_power_of_two_closed_form():
+    """amax = 448 * 2^j gives the scale 2^j exactly, so the codes are those of
+    x * 2^-j (an exact scaling) encoded by torch's e4m3fn cast."""
+    x = workloads.bf16_normal((2048,), 1.0, seed=13, name="ptb")
+    xt = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float()
+    for j in (-3, 0, 4):
+        c, s = per_tensor.pt_quantize_given_amax(x, 448.0 * 2.0 ** j)
+        assert s == np.float32(2.0 ** j)
+        ref = (xt * 2.0 ** -j).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(c, ref)
+
+
 def test_dequant_error_relative():
     x = workloads.bf16_normal((8192,), 1.0, seed=8, name="pt4")
     codes, s = per_tensor.pt_quantize(x)
