@@ -416,6 +416,15 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
     (px, sx), t_px = timed(mxq.fp8_quantize_per_tensor, X)
     (pw, sw), t_pw = timed(mxq.fp8_quantize_per_tensor, W)
     _, t_pg = timed(mxq.fp8_gemm_per_tensor, px, sx, pw, sw)
+    # The product's output quantized per tensor for the next product: the
+    # amax from a pass over C, or from the GEMM's epilogue (no amax pass).
+    c_pt = mxq.fp8_gemm_per_tensor(px, sx, pw, sw)
+    (cq, cs), t_cq2 = timed(mxq.fp8_quantize_per_tensor, c_pt)
+    (_, c_amax), t_pga = timed(mxq.fp8_gemm_per_tensor_amax, px, sx, pw, sw)
+    (cq1, cs1), t_cq1 = timed(mxq.fp8_quantize_per_tensor_amax, c_pt, c_amax)
+    assert torch.equal(cq, cq1) and torch.equal(cs, cs1)   # same codes either way
+    nC = c_pt.numel()
+    del c_pt, cq, cs, cq1, cs1
     (bx, bsx), t_bx = timed(mxq.fp8_quantize_blockwise_act, X)
     (bwq, bsw), t_bw = timed(mxq.fp8_quantize_blockwise_weight, W)
     _, t_bg = timed(mxq.fp8_gemm_blockwise, bx, bsx, bwq, bsw)
@@ -490,6 +499,14 @@ def dense_component(torch, mxq, workloads, to_dev, seed, reps=5):
         "per_tensor_quant_X": {"us": t_px * 1e3, "GB_per_s_algorithmic": gb(nX, 3, t_px)},
         "per_tensor_quant_W": {"us": t_pw * 1e3, "GB_per_s_algorithmic": gb(nW, 3, t_pw)},
         "per_tensor_gemm_fwd": {"us": t_pg * 1e3, "TFLOP_per_s": flops / (t_pg * 1e-3) / 1e12},
+        "per_tensor_output_quant": {
+            "note": "C 8192x10944 quantized per tensor for a next product: amax pass + encode, "
+                    "or the amax from the GEMM's epilogue and the encode alone",
+            "gemm_us": t_pg * 1e3, "gemm_with_epilogue_amax_us": t_pga * 1e3,
+            "quant_two_pass_us": t_cq2 * 1e3, "quant_given_amax_us": t_cq1 * 1e3,
+            "chain_two_pass_us": (t_pg + t_cq2) * 1e3,
+            "chain_epilogue_amax_us": (t_pga + t_cq1) * 1e3,
+            "quant_given_amax_GB_per_s": gb(nC, 3, t_cq1)},
         "blockwise_quant_X_1x128": {"us": t_bx * 1e3, "GB_per_s": gb(nX, 3 + 4 / 128, t_bx)},
         "blockwise_quant_W_128x128": {"us": t_bw * 1e3, "GB_per_s": gb(nW, 3, t_bw)},
         "blockwise_gemm_fwd": {"us": t_bg * 1e3, "TFLOP_per_s": flops / (t_bg * 1e-3) / 1e12},

@@ -575,16 +575,27 @@ __global__ __launch_bounds__(kPtThreads) void k_pt_amax(const uint16_t* __restri
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
+// amax_in: the tensor's amax given by the caller (then partial is unused);
+// the rule is the same: s = amax / 448 when amax is finite and > 0, else 1.
 __global__ __launch_bounds__(kPtThreads) void k_pt_quant(const uint16_t* __restrict__ x, int64_t n,
                                                          const uint32_t* __restrict__ partial, int nparts,
-                                                         uint8_t* __restrict__ q, float* __restrict__ scale_out) {
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale_out,
+                                                         const float* __restrict__ amax_in) {
   __shared__ uint32_t red[kPtThreads / 64];
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = m > partial[i] ? m : partial[i];
-  m = block_max_u32(m, red);
-  const bool nonfinite = m >= 0x7F80u;
+  bool nonfinite;
   float s = 1.0f;
-  if (!nonfinite && m != 0u) s = __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f);
+  if (amax_in) {
+    const float a = *amax_in;
+    const uint32_t ab = __builtin_bit_cast(uint32_t, a) & 0x7FFFFFFFu;
+    nonfinite = ab >= 0x7F800000u;                  // NaN or Inf
+    if (!nonfinite && a > 0.0f) s = __fdiv_rn(a, 448.0f);
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = m > partial[i] ? m : partial[i];
+    m = block_max_u32(m, red);
+    nonfinite = m >= 0x7F80u;
+    if (!nonfinite && m != 0u) s = __fdiv_rn(__builtin_bit_cast(float, m << 16), 448.0f);
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = s;
   const bool direct = s < 1.17549435e-38f;        // subnormal scale: divide directly
   const float r = __frcp_rn(s);
@@ -1324,7 +1335,21 @@ extern "C" int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q,
   int st = launch_status();
   if (st != MXQ_OK) return st;
   hipLaunchKernelGGL(k_pt_quant, dim3((uint32_t)blocks), dim3(kPtThreads), 0, stream, x, n,
-                     partial, (int)blocks, q, scale);
+                     partial, (int)blocks, q, scale, nullptr);
+  return launch_status();
+}
+
+extern "C" int fp8_quantize_per_tensor_amax(const uint16_t* x, int64_t n, const float* amax,
+                                            uint8_t* q, float* scale, hipStream_t stream) {
+  if (n < 0) return MXQ_ERR_SHAPE;
+  if (!scale || !amax) return MXQ_ERR_NULL;
+  if (n > 0 && (!x || !q)) return MXQ_ERR_NULL;
+  if (n > 0 && (!aligned(x, 16) || !aligned(q, 16))) return MXQ_ERR_ALIGN;
+  int64_t blocks = (n / 8 + kPtThreads - 1) / kPtThreads;
+  if (blocks < 1) blocks = 1;
+  if (blocks > kPtBlocks) blocks = kPtBlocks;
+  hipLaunchKernelGGL(k_pt_quant, dim3((uint32_t)blocks), dim3(kPtThreads), 0, stream, x, n,
+                     nullptr, 0, q, scale, amax);
   return launch_status();
 }
 

@@ -49,6 +49,7 @@ _SIGS = {
     "mx_quantize_dual": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p, _i64,
                                         _p, _i64, _i64, _p, _i64, _p, _p]),
     "fp8_quantize_per_tensor": (ctypes.c_int, [_p, _i64, _p, _p, _p, _sz, _p]),
+    "fp8_quantize_per_tensor_amax": (ctypes.c_int, [_p, _i64, _p, _p, _p, _p]),
     "fp8_quantize_per_group": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p, _i64, _p,
                                               _p, _sz, _p]),
     "fp8_quantize_per_group_noalloc": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i32, _p,
@@ -57,6 +58,8 @@ _SIGS = {
                                _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
     "fp8_gemm_per_tensor": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
                                            _p, _i64, ctypes.c_int, ctypes.c_int, _p]),
+    "fp8_gemm_per_tensor_amax": (ctypes.c_int, [_p, _p, _i64, _p, _p, _i64, _i64, _i64, _i64,
+                                                _p, _i64, ctypes.c_int, ctypes.c_int, _p, _p]),
     "mx_grouped_gemm": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _i64, _i64, _i64, _p, _i32,
                                        _i64, _i64, _i64, _p, _i64, ctypes.c_int,
                                        ctypes.c_int, _p]),
@@ -292,6 +295,20 @@ def fp8_quantize_per_tensor(x, q=None, scale=None, workspace=None):
     return q, scale
 
 
+def fp8_quantize_per_tensor_amax(x, amax, q=None, scale=None):
+    """fp8_quantize_per_tensor with the amax given (float32 [1] on the device),
+    e.g. from fp8_gemm_per_tensor_amax.  Returns (codes uint8, scale float32 [1])."""
+    x = _bf16_bits(x)
+    n = x.numel()
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(load().fp8_quantize_per_tensor_amax(_ptr(x), n, _ptr(amax), _ptr(q), _ptr(scale),
+                                               _stream()))
+    return q, scale
+
+
 def fp8_quantize_per_group(x, offsets, q=None, scales=None, workspace=None):
     """Per-group (per-expert) current-scaling E4M3 of a BF16 [M, K] matrix
     whose rows [offsets[e], offsets[e+1]) form group e (offsets int64 [E+1]
@@ -454,6 +471,22 @@ def fp8_gemm_per_tensor(a, a_scale, b, b_scale, out_dtype=OUT_BF16, accum=ACC_MF
                                       _ptr(b_scale), b.stride(0), M, N, K, _ptr(c),
                                       c.stride(0), out_dtype, accum, _stream()))
     return c
+
+
+def fp8_gemm_per_tensor_amax(a, a_scale, b, b_scale, out_dtype=OUT_BF16,
+                             accum=ACC_MFMA_FP8, c=None, c_amax=None):
+    """fp8_gemm_per_tensor that also returns max |C| (float32 [1], from the
+    epilogue): (C, amax)."""
+    M, K = a.shape
+    N = b.shape[0]
+    c = _out(M, N, out_dtype, a.device, c)
+    if c_amax is None:
+        c_amax = torch.empty(1, dtype=torch.float32, device=a.device)
+    _check(load().fp8_gemm_per_tensor_amax(_ptr(a), _ptr(a_scale), a.stride(0), _ptr(b),
+                                           _ptr(b_scale), b.stride(0), M, N, K, _ptr(c),
+                                           c.stride(0), out_dtype, accum, _ptr(c_amax),
+                                           _stream()))
+    return c, c_amax
 
 
 def mx_grouped_gemm(a, a_scale, b, b_scale, offsets, out_dtype=OUT_BF16,

@@ -208,6 +208,22 @@ MXQ_API int fp8_quantize_per_tensor(const uint16_t* x, int64_t n, uint8_t* q, fl
                             hipStream_t stream);
 
 /*
+ * fp8_quantize_per_tensor with the tensor's amax given instead of found by a
+ * first pass over x ([FPBLOG] §七.2: the amax pass is current scaling's extra
+ * read, and the producing matmul's epilogue can supply the amax, as
+ * fp8_gemm_per_tensor_amax does).
+ *   amax  : device float[1]; the scale is the rule above applied to it
+ *           (s = amax / 448 in FP32 when amax is finite and > 0, else 1; a NaN
+ *           or infinite amax turns NaN codes into 0x7F | sign and saturates
+ *           +-Inf, as the two-pass call does).  The codes and scale equal
+ *           fp8_quantize_per_tensor's when amax is the true max |x|.
+ *   x, q  : as for fp8_quantize_per_tensor; scale: device float[1] receiving s.
+ * No workspace.  n == 0 writes only the scale.
+ */
+MXQ_API int fp8_quantize_per_tensor_amax(const uint16_t* x, int64_t n, const float* amax,
+                                 uint8_t* q, float* scale, hipStream_t stream);
+
+/*
  * Per-group (per-expert) current-scaling FP8 E4M3 ([HP329] §3 format table:
  * a grouped tensor keeps one FP32 scale per leading group; §3.2: 3-D grouped
  * weights take a per-leading-group scale, each from the rule above; [TTNPU]
@@ -377,6 +393,24 @@ MXQ_API int fp8_gemm_per_tensor(const uint8_t* a, const float* a_scale, int64_t 
                         int64_t M, int64_t N, int64_t K,
                         void* c, int64_t ldc, int out_dtype, int accum,
                         hipStream_t stream);
+
+/*
+ * fp8_gemm_per_tensor that also takes the current-scaling amax of its output
+ * in the epilogue ([FPBLOG] §七.2: the amax can come from the producing
+ * matmul, so quantizing C per tensor needs no amax pass; [HP329] §3.2 current
+ * scaling).  Same arguments and requirements as fp8_gemm_per_tensor, plus
+ *   c_amax : device float[1], 4-byte aligned.  Cleared, then set to the
+ *            largest |C| over the M x N outputs as stored (rounded to the
+ *            output type): NaN if an output is NaN, else +Inf if one is
+ *            infinite; 0 when M, N or K is 0.
+ * fp8_quantize_per_tensor_amax(C, ..., c_amax, ...) then gives exactly the
+ * codes and scale of fp8_quantize_per_tensor(C, ...).
+ */
+MXQ_API int fp8_gemm_per_tensor_amax(const uint8_t* a, const float* a_scale, int64_t lda,
+                             const uint8_t* b, const float* b_scale, int64_t ldb,
+                             int64_t M, int64_t N, int64_t K,
+                             void* c, int64_t ldc, int out_dtype, int accum, float* c_amax,
+                             hipStream_t stream);
 
 /*
  * Blockwise FP8, the comparison recipe ([FPBLOG] §七.3, DeepSeek-V3): E4M3

@@ -130,6 +130,14 @@ int main() {
   EXPECT(fp8_quantize_per_tensor(X, 100, P, Fp, P, 4, nullptr), MXQ_ERR_WORKSPACE);
   EXPECT(fp8_quantize_per_tensor(X, 100, P, Fp, P, 4096, nullptr), HIP);
   EXPECT(fp8_quantize_per_tensor(X, HUGE_, P, Fp, P, 4096, nullptr), HIP);
+  EXPECT(fp8_quantize_per_tensor_amax(X, -5, Fp, P, Fp, nullptr), MXQ_ERR_SHAPE);
+  EXPECT(fp8_quantize_per_tensor_amax(X, 100, nullptr, P, Fp, nullptr), MXQ_ERR_NULL);
+  EXPECT(fp8_quantize_per_tensor_amax(X, 100, Fp, P, nullptr, nullptr), MXQ_ERR_NULL);
+  EXPECT(fp8_quantize_per_tensor_amax(nullptr, 100, Fp, P, Fp, nullptr), MXQ_ERR_NULL);
+  EXPECT(fp8_quantize_per_tensor_amax(X + 1, 100, Fp, P, Fp, nullptr), MXQ_ERR_ALIGN);
+  EXPECT(fp8_quantize_per_tensor_amax(nullptr, 0, Fp, nullptr, Fp, nullptr), HIP);
+  EXPECT(fp8_quantize_per_tensor_amax(X, 100, Fp, P, Fp, nullptr), HIP);
+  EXPECT(fp8_quantize_per_tensor_amax(X, HUGE_, Fp, P, Fp, nullptr), HIP);
   const size_t ws = mxq_workspace_size(MXQ_WS_PER_GROUP, 64, 4, 0, 0);
   EXPECT((int)(ws == (64 + 4) * 4), 1);
   EXPECT((int)(mxq_workspace_size(MXQ_WS_PER_GROUP, -1, 4, 0, 0) == 0), 1);
@@ -169,6 +177,16 @@ int main() {
     EXPECT(mx_gemm(P, P, HUGE_ / 32 * 32, HUGE_, P, P, HUGE_ / 32 * 32, HUGE_, 4, 4,
                    HUGE_ / 32 * 32, P, 4, 0, acc, nullptr), MXQ_ERR_SHAPE);
     EXPECT(fp8_gemm_per_tensor(P, Fp, 32, P, Fp, 32, 4, 4, 32, P, 4, 1, acc, nullptr), HIP);
+    EXPECT(fp8_gemm_per_tensor_amax(P, Fp, 32, P, Fp, 32, 4, 4, 32, P, 4, 1, acc, nullptr,
+                                    nullptr), MXQ_ERR_NULL);
+    EXPECT(fp8_gemm_per_tensor_amax(P, Fp, 32, P, Fp, 32, 4, 4, 32, P, 4, 1, acc,
+                                    reinterpret_cast<float*>(P + 2), nullptr), MXQ_ERR_ALIGN);
+    EXPECT(fp8_gemm_per_tensor_amax(P, Fp, 32, P, Fp, 32, 4, 4, 33, P, 4, 1, acc, Fp, nullptr),
+           MXQ_ERR_SHAPE);
+    EXPECT(fp8_gemm_per_tensor_amax(P, Fp, 32, P, Fp, 32, 0, 4, 32, P, 4, 1, acc, Fp, nullptr),
+           HIP);                                              // clears the amax: a launch
+    EXPECT(fp8_gemm_per_tensor_amax(P, Fp, 32, P, Fp, 32, 4, 4, 32, P, 4, 1, acc, Fp, nullptr),
+           HIP);
     EXPECT(fp8_gemm_per_tensor(P, Fp, 32, P, Fp, 32, HUGE_, HUGE_, 32, P, HUGE_, 1, acc, nullptr),
            MXQ_ERR_SHAPE);
     EXPECT(mx_grouped_gemm(P, P, 32, 1, P, P, 32, 1, 256, 8, O, 4, 8, 8, 32, P, 8, 0, acc, nullptr),

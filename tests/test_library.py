@@ -87,6 +87,16 @@ def test_host_validation_errors(host_only_lib):
     assert lib.mx_grouped_gemm_wgrad(P, P, 40, 2, P, P, 32, 1, P, 2, 8, 8, P, 8, 0, 0, None) == 3
     assert lib.fp8_quantize_per_tensor(P, -5, P, P, P, 4096, None) == 2
     assert lib.fp8_quantize_per_tensor(P, 100, P, P, P, 4, None) == 5          # workspace
+    # given amax: (x, n, amax, q, scale, stream)
+    assert lib.fp8_quantize_per_tensor_amax(P, -5, P, P, P, None) == 2
+    assert lib.fp8_quantize_per_tensor_amax(P, 100, None, P, P, None) == 1     # amax
+    assert lib.fp8_quantize_per_tensor_amax(P, 100, P, P, None, None) == 1     # scale
+    assert lib.fp8_quantize_per_tensor_amax(P + 2, 100, P, P, P, None) == 3    # misaligned x
+    # GEMM with the output's amax: (a, sa, lda, b, sb, ldb, M, N, K, c, ldc, out, acc, amax, s)
+    assert lib.fp8_gemm_per_tensor_amax(P, P, 32, P, P, 32, 4, 4, 32, P, 4, 0, 0, None, None) == 1
+    assert lib.fp8_gemm_per_tensor_amax(P, P, 32, P, P, 32, 4, 4, 32, P, 4, 0, 0, P + 2, None) == 3
+    assert lib.fp8_gemm_per_tensor_amax(P, P, 32, P, P, 32, 4, 4, 32, P, 4, 2, 0, P, None) == 4
+    assert lib.fp8_gemm_per_tensor_amax(P, P, 32, P, P, 32, 4, 4, 33, P, 4, 0, 0, P, None) == 2
     assert lib.mxq_workspace_size(0, 100, 0, 0, 0) > 0
     assert lib.mxq_workspace_size(0, 0, 0, 0, 0) == 0
     assert lib.mxq_validate_offsets(None, 4, 10, None) == 1
